@@ -1,0 +1,283 @@
+"""Oracle for the top-2 MoE FFN layer -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow CPU reference of what the layer computes. Only the test suite, the
+graft smoke check and the benchmark's CPU-baseline leg may import it; the
+product path (the HIP library and its Python binding) never does.
+
+Every function follows the n4n.ai page "How does Grok-1 use a
+mixture-of-experts design?" (cited below as "the page"), written from the
+page's description, not from its code listings. Precision:
+  * the router product and the top-k decision are taken in float32, the
+    precision the GPU kernel decides in; the same product is also formed in
+    float64 to measure how close each decision was (tie flags);
+  * everything else (softmax weights, expert FFN, combine) is float64 on the
+    exact values the GPU consumes (bf16 widened exactly, int8 as q * s).
+Library primitives used as steps: numpy matmul, argsort, exp.
+
+Pins: tests/test_oracle_*.py check each function against brute force,
+closed forms and the page's printed sizes (no function here is unpinned).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# storage widening (the oracle's own; exact)
+# --------------------------------------------------------------------------
+
+
+def widen_bf16_bits(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (a bf16 is the top half of a float32)."""
+    b = np.asarray(b)
+    if b.dtype != np.uint16:
+        raise TypeError("bf16 values are passed as uint16 bit patterns")
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def widen(a: np.ndarray, kind: str, scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Stored matrix -> float64. kind: 'f32' | 'bf16' | 'i8' (rows scaled by scale[row])."""
+    if kind == "f32":
+        return np.asarray(a, np.float32).astype(np.float64)
+    if kind == "bf16":
+        return widen_bf16_bits(a)
+    if kind == "i8":
+        if scale is None:
+            raise ValueError("int8 weights need their per-row scales")
+        # q * s is exact in float64 (8-bit times 24-bit significands)
+        return np.asarray(a, np.int8).astype(np.float64) * \
+            np.asarray(scale, np.float32).astype(np.float64)[:, None]
+    raise ValueError(kind)
+
+
+# --------------------------------------------------------------------------
+# router (the page, section "Routing: top-2 without auxiliary loss",
+# grok_router_forward; and "The high-level architecture", GrokMoELayer.forward)
+# --------------------------------------------------------------------------
+
+
+def router_logits(x64: np.ndarray, wr: np.ndarray):
+    """Bias-free router linear: logits[t,e] = sum_h x[t,h] * Wr[e,h].
+
+    The page's router is nn.Linear(hidden, 8, bias=False) applied to the
+    flattened tokens. Returns (l32, l64): the product in float32 (used for the
+    decision) and in float64 (used for the softmax weights and tie gaps)."""
+    wr32 = np.asarray(wr, np.float32)
+    l32 = (x64.astype(np.float32) @ wr32.T).astype(np.float32)
+    l64 = x64 @ wr32.astype(np.float64).T
+    return l32, l64
+
+
+@dataclass
+class Routing:
+    idx: np.ndarray      # [T,k] int32, slot 0 = larger logit
+    w: np.ndarray        # [T,k] float64 softmax over the k selected logits
+    tie: np.ndarray      # [T] bool: a decision gap below the tie tolerance
+    l32: np.ndarray
+    l64: np.ndarray
+
+
+def top_k_softmax(l32: np.ndarray, l64: np.ndarray, k: int,
+                  tie_tol: float = 1e-4) -> Routing:
+    """Top-k experts per token and a softmax over only the selected logits.
+
+    The page takes torch.topk over the logits (k = 2, sorted, largest first)
+    and then a softmax over the k selected values. Equal logits: the lower
+    expert index ranks first. A token is flagged as a tie when any of the
+    decisive float64 gaps (between ranks j and j+1 for j < k, i.e. the slot
+    order and the k / k+1 boundary) is below tie_tol * max(1, max|logit|)."""
+    T, E = l32.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # stable sort of the negated values: equal logits keep ascending index
+    order = np.argsort(-l32, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(l64, order[:, :k], axis=1)
+    z = np.exp(sel - sel[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)
+
+    ranked64 = np.take_along_axis(l64, order, axis=1)
+    last = min(k, E - 1)
+    gaps = ranked64[:, :last] - ranked64[:, 1:last + 1]
+    scale = np.maximum(1.0, np.abs(l64).max(axis=1)) if E > 0 else 1.0
+    tie = (gaps < tie_tol * scale[:, None]).any(axis=1) if last > 0 else np.zeros(T, bool)
+    return Routing(idx, w, tie, l32, l64)
+
+
+# --------------------------------------------------------------------------
+# dispatch with capacity (the page, grok_router_forward's one-hot dispatch
+# mask and the capacity-aware dropping it applies when the factor is finite;
+# capacity sizing in the paragraph after it: factor x mean load per expert)
+# --------------------------------------------------------------------------
+
+
+def capacity(T: int, k: int, E: int, capacity_factor) -> Optional[int]:
+    """Per-expert capacity ceil(cf * (T*k) / E), evaluated in double precision
+    in that order; None (no limit) when the factor is None, <= 0 or infinite.
+
+    The page sizes capacity as the factor times the per-expert share of the
+    routed work; the mean load per expert is T*k/E (section "Tradeoffs",
+    expert batch size analysis)."""
+    if capacity_factor is None:
+        return None
+    cf = float(np.float32(capacity_factor))
+    if not (cf > 0) or math.isinf(cf):
+        return None
+    return int(math.ceil(cf * float(T * k) / float(E)))
+
+
+@dataclass
+class Dispatch:
+    counts: np.ndarray    # [E] int32, all requests per expert (before the drop)
+    offsets: np.ndarray   # [E+1] int32, exclusive scan of kept rows per expert
+    perm: np.ndarray      # [T*k] int32, row -> assignment t*k+j; tail -1
+    slot_row: np.ndarray  # [T*k] int32, assignment -> row, -1 if dropped
+    dropped: np.ndarray   # [T*k] uint8
+    cap: Optional[int]
+
+
+def dispatch(idx: np.ndarray, E: int, capacity_factor=None) -> Dispatch:
+    """Group assignments (t, j) by expert in token order and drop over capacity.
+
+    Walks tokens in index order keeping one running counter per expert: an
+    assignment's rank in its expert is the number of earlier tokens that chose
+    that expert; it is kept iff rank < capacity. Kept rows of expert e occupy
+    rows offsets[e] .. offsets[e+1]-1 in rank order."""
+    T, k = idx.shape
+    cap = capacity(T, k, E, capacity_factor)
+    cnt = [0] * E
+    rank = np.empty((T, k), np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            rank[t, j] = cnt[e]
+            cnt[e] += 1
+    counts = np.asarray(cnt, np.int32)
+    kept = counts if cap is None else np.minimum(counts, cap)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(kept)
+    perm = np.full(T * k, -1, np.int32)
+    slot_row = np.full(T * k, -1, np.int32)
+    dropped = np.zeros(T * k, np.uint8)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            a = t * k + j
+            if cap is None or rank[t, j] < cap:
+                r = int(offsets[e] + rank[t, j])
+                perm[r] = a
+                slot_row[a] = r
+            else:
+                dropped[a] = 1
+    return Dispatch(counts, offsets, perm, slot_row, dropped, cap)
+
+
+# --------------------------------------------------------------------------
+# expert FFN (the page, section "Expert implementation: SwiGLU at scale",
+# SwiGLUExpert: w_down(silu(w_gate x) * w_up x), all bias-free)
+# --------------------------------------------------------------------------
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_expert(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray,
+                  wd64: np.ndarray) -> np.ndarray:
+    """One expert on rows x [m,H]: (silu(x Wg^T) * (x Wu^T)) Wd^T -> [m,H]."""
+    g = x64 @ wg64.T
+    u = x64 @ wu64.T
+    return (silu(g) * u) @ wd64.T
+
+
+# --------------------------------------------------------------------------
+# the layer (the page, GrokMoELayer.forward: flatten, router, top-2, softmax
+# over the selected logits, per-expert compute and weighted combine; the EP
+# pseudocode in "Expert parallelism vs. tensor parallelism" multiplies each
+# expert's output by the token's weight for that expert and skips experts
+# that received no token)
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class LayerResult:
+    routing: Routing
+    disp: Dispatch
+    tokens: np.ndarray    # token ids whose outputs were evaluated
+    out: np.ndarray       # [len(tokens), H] float64
+
+
+def layer_forward(x: np.ndarray, act: str, wr: np.ndarray,
+                  wg: Sequence, wu: Sequence, wd: Sequence, wdt: str,
+                  k: int = 2, capacity_factor=None,
+                  sg=None, su=None, sd=None,
+                  tokens: Optional[np.ndarray] = None,
+                  tie_tol: float = 1e-4) -> LayerResult:
+    """Whole-layer forward. Routing and dispatch run over all T tokens (the
+    capacity decision depends on every earlier token); the expert FFN and the
+    combine run only for `tokens` (all tokens when None).
+
+    out[t] = sum over kept slots j of w[t,j] * expert_{idx[t,j]}(x[t]),
+    slot 0 first; a token whose slots were all dropped gets a zero row."""
+    x64 = widen(x, act)
+    T, H = x64.shape
+    E = np.asarray(wr).shape[0]
+    l32, l64 = router_logits(x64, wr)
+    routing = top_k_softmax(l32, l64, k, tie_tol)
+    disp = dispatch(routing.idx, E, capacity_factor)
+
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    # expert output of every kept (sample position, slot) pair
+    y_of = {}
+    for e in range(E):
+        pairs = [(p, j) for p, t in enumerate(tokens) for j in range(k)
+                 if routing.idx[t, j] == e and disp.slot_row[t * k + j] >= 0]
+        if not pairs:
+            continue          # an expert that received no tokens is skipped
+        s_g = None if sg is None else sg[e]
+        s_u = None if su is None else su[e]
+        s_d = None if sd is None else sd[e]
+        y = swiglu_expert(x64[[int(tokens[p]) for p, _ in pairs]],
+                          widen(wg[e], wdt, s_g), widen(wu[e], wdt, s_u),
+                          widen(wd[e], wdt, s_d))
+        for i, pj in enumerate(pairs):
+            y_of[pj] = y[i]
+    # weighted combine back to token order, slot 0 first
+    out = np.zeros((len(tokens), H), np.float64)
+    for p, t in enumerate(tokens):
+        for j in range(k):
+            if (p, j) in y_of:
+                out[p] += routing.w[t, j] * y_of[(p, j)]
+    return LayerResult(routing, disp, tokens, out)
+
+
+# --------------------------------------------------------------------------
+# sizes and statistics printed or used on the page
+# --------------------------------------------------------------------------
+
+
+def expert_batch_size(global_batch: int, seq_len: int, num_experts: int = 8,
+                      top_k: int = 2) -> float:
+    """Mean assignments per expert, batch*seq*k/E (section "Tradeoffs")."""
+    return global_batch * seq_len * top_k / num_experts
+
+
+def expert_params(hidden: int, expert_dim: int) -> int:
+    """Weights of one SwiGLU expert: gate and up [F,H] plus down [H,F]."""
+    return 3 * hidden * expert_dim
+
+
+def expert_utilization(idx: np.ndarray, E: int) -> np.ndarray:
+    """Per-expert share of the top-k picks normalised so a balanced router
+    scores 1.0 for every expert: counts / (T*k) * E. (The page's utilisation
+    snippet divides by the number of picks and then multiplies by E/2, which
+    gives 0.5 for a balanced router, not the 1.0 its comment claims; this is
+    the normalisation the comment describes.)"""
+    idx = np.asarray(idx)
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.float64)
+    return counts / idx.size * E

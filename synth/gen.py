@@ -1,0 +1,128 @@
+"""Host-side seeded generation (numpy PCG64) of layer inputs.
+
+Draw order, all from one numpy Generator(PCG64(seed)):
+  x [T,H] ~ N(0,1); router W [E,H] ~ N(0,1/H); then for e = 0..E-1:
+  W_gate[e] [F,H] ~ N(0,1/H), W_up[e] [F,H] ~ N(0,1/H), W_down[e] [H,F] ~ N(0,1/F).
+Draws are float32. Storage conversions:
+  bf16 : round-to-nearest-even of the float32 draw, kept as uint16 bit patterns;
+  i8   : per output row, s = max|w| / 127 and q = clip(rint(w / s), -127, 127).
+The router weight always stays float32. A skewed router adds skew[e] * u to
+row e, u the unit vector along the column mean of x as stored.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+from .configs import LayerConfig
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits.
+
+    Inputs are finite (no NaN handling is needed for Gaussian draws)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 exactly."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def quantize_int8_rows(w: np.ndarray):
+    """Per-output-row absmax int8 quantisation of a float32 matrix [N, K].
+
+    Returns (q int8 [N,K], s float32 [N]) with w ~= q * s[:, None]."""
+    w = np.asarray(w, dtype=np.float32)
+    s = (np.max(np.abs(w), axis=1) / np.float32(127.0)).astype(np.float32)
+    s_safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(w / s_safe[:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+@dataclass
+class HostInputs:
+    """Arrays of one layer instance as the layer stores them.
+
+    x   : float32 [T,H] (act f32) or uint16 bf16 bits [T,H] (act bf16)
+    wr  : float32 [E,H]
+    wg, wu : [E,F,H]; wd : [E,H,F]  -- float32, uint16 bf16 bits, or int8
+    sg, su : float32 [E,F]; sd : float32 [E,H]  -- only for int8 weights
+    """
+    cfg: LayerConfig
+    x: np.ndarray
+    wr: np.ndarray
+    wg: np.ndarray
+    wu: np.ndarray
+    wd: np.ndarray
+    sg: Optional[np.ndarray] = None
+    su: Optional[np.ndarray] = None
+    sd: Optional[np.ndarray] = None
+
+    def arrays(self) -> Dict[str, np.ndarray]:
+        d = dict(x=self.x, wr=self.wr, wg=self.wg, wu=self.wu, wd=self.wd)
+        if self.sg is not None:
+            d.update(sg=self.sg, su=self.su, sd=self.sd)
+        return d
+
+
+def _store_weight(w32: np.ndarray, wdt: str):
+    if wdt == "f32":
+        return w32, None
+    if wdt == "bf16":
+        return bf16_bits_from_f32(w32), None
+    if wdt == "i8":
+        return quantize_int8_rows(w32)
+    raise ValueError(wdt)
+
+
+def x_as_f32(x: np.ndarray, act: str) -> np.ndarray:
+    return f32_from_bf16_bits(x) if act == "bf16" else np.asarray(x, np.float32)
+
+
+def skew_direction(x_stored_f32: np.ndarray) -> np.ndarray:
+    """Unit vector (float32) along the column mean of the activations."""
+    m = x_stored_f32.astype(np.float64).mean(axis=0)
+    n = np.linalg.norm(m)
+    return (m / n).astype(np.float32) if n > 0 else np.zeros_like(m, np.float32)
+
+
+def generate_host(cfg: LayerConfig, seed: Optional[int] = None) -> HostInputs:
+    """Draw one layer instance on the host (sizes up to a few hundred MB)."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
+    T, H, F, E = cfg.T, cfg.H, cfg.F, cfg.E
+    f32 = np.float32
+    x32 = rng.standard_normal((T, H), dtype=f32)
+    wr = (rng.standard_normal((E, H), dtype=f32) * f32(1.0 / np.sqrt(H))).astype(f32)
+    x = bf16_bits_from_f32(x32) if cfg.act == "bf16" else x32
+
+    wdt_np = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[cfg.wdt]
+    wg = np.empty((E, F, H), wdt_np)
+    wu = np.empty((E, F, H), wdt_np)
+    wd = np.empty((E, H, F), wdt_np)
+    sg = su = sd = None
+    if cfg.wdt == "i8":
+        sg = np.empty((E, F), f32)
+        su = np.empty((E, F), f32)
+        sd = np.empty((E, H), f32)
+    for e in range(E):
+        g = rng.standard_normal((F, H), dtype=f32) * f32(1.0 / np.sqrt(H))
+        u = rng.standard_normal((F, H), dtype=f32) * f32(1.0 / np.sqrt(H))
+        d = rng.standard_normal((H, F), dtype=f32) * f32(1.0 / np.sqrt(F))
+        wg[e], s0 = _store_weight(g.astype(f32), cfg.wdt)
+        wu[e], s1 = _store_weight(u.astype(f32), cfg.wdt)
+        wd[e], s2 = _store_weight(d.astype(f32), cfg.wdt)
+        if cfg.wdt == "i8":
+            sg[e], su[e], sd[e] = s0, s1, s2
+
+    if cfg.skew:
+        u = skew_direction(x_as_f32(x, cfg.act))
+        for e, a in enumerate(cfg.skew):
+            wr[e] = (wr[e] + f32(a) * u).astype(f32)
+
+    return HostInputs(cfg, x, wr, wg, wu, wd, sg, su, sd)

@@ -1,0 +1,47 @@
+"""Checks of the seeded input generator (CPU only)."""
+import numpy as np
+import torch
+
+import synth
+
+
+def test_bf16_rounding_matches_torch():
+    a = np.random.default_rng(0).standard_normal(100_000).astype(np.float32) * 3
+    a[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0]  # ties to even
+    ours = synth.bf16_bits_from_f32(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(synth.f32_from_bf16_bits(ours),
+                          torch.from_numpy(a).to(torch.bfloat16).float().numpy())
+
+
+def test_int8_quantisation_rule():
+    w = np.random.default_rng(1).standard_normal((50, 300)).astype(np.float32)
+    q, s = synth.quantize_int8_rows(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    err = np.abs(q.astype(np.float64) * s[:, None] - w)
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-5))
+
+
+def test_distributions_and_determinism():
+    cfg = synth.get_config("tiny").with_(T=512, F=1024)
+    a = synth.generate_host(cfg)
+    b = synth.generate_host(cfg)
+    for k, v in a.arrays().items():
+        assert np.array_equal(v, b.arrays()[k]), k
+    assert abs(a.x.std() - 1) < 0.02
+    assert abs(a.wr.std() * np.sqrt(cfg.H) - 1) < 0.1
+    assert abs(a.wg.std() * np.sqrt(cfg.H) - 1) < 0.02
+    assert abs(a.wd.std() * np.sqrt(cfg.F) - 1) < 0.02
+
+
+def test_storage_dtypes():
+    for name, xt, wt in [("p_bf16", np.uint16, np.uint16), ("p_i8", np.uint16, np.int8),
+                         ("p_f32", np.float32, np.float32)]:
+        cfg = synth.get_config(name).with_(T=8)
+        inp = synth.generate_host(cfg)
+        assert inp.x.dtype == xt and inp.wg.dtype == wt and inp.wr.dtype == np.float32
+        assert inp.wg.shape == (cfg.E, cfg.F, cfg.H) and inp.wd.shape == (cfg.E, cfg.H, cfg.F)
+        if cfg.wdt == "i8":
+            assert inp.sg.shape == (cfg.E, cfg.F) and inp.sd.shape == (cfg.E, cfg.H)
