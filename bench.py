@@ -1,0 +1,289 @@
+"""Benchmark of the top-2 MoE FFN layer (Grok-1 shape) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skew|capacity]
+
+A step is one moe_layer_forward call: router + top-2 + softmax, dispatch,
+gate/up GEMM with SwiGLU, down GEMM and combine, over one batch of seeded
+synthetic inputs already resident in HBM. W untimed steps, then K steps
+timed with HIP events between two device synchronisations. Prints ONE JSON
+line on stdout (logs go to stderr):
+  value      tokens/s of the whole layer at the chosen workload (default:
+             the Grok-1-shape decode batch, T = 8);
+  roofline   the dominant kernel (gate/up GEMM) against HBM (decode) or bf16
+             MFMA peak (prefill): algorithmic bytes or flops per launch over
+             its mean duration, timed with events around that launch in a
+             stage-by-stage pass over K more steps;
+  prefill    the same layer at T = 8192 (one full context), MFMA-bound;
+  cpu_baseline  the oracle (numpy float64, test infrastructure) on a bounded
+             sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE-layer tokens/sec at Grok-1 shape; % HBM BW (decode) / % MFMA peak (prefill)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gateup_decode": ["sparse_moe_transformer_top_amd/csrc/ffn_decode.hip",
+                      "sparse_moe_transformer_top_amd/csrc/common.h"],
+    "gateup_tiled": ["sparse_moe_transformer_top_amd/csrc/ffn_tiled.hip",
+                     "sparse_moe_transformer_top_amd/csrc/common.h",
+                     "sparse_moe_transformer_top_amd/csrc/grouped.h"],
+}
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel calibration), if recorded for the
+    current source of the kernel; None otherwise."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{kernel}/{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Layer:
+    """Inputs, workspace and the step functions of one workload."""
+
+    def __init__(self, cfg, dev, torch, moe, weights=None):
+        from synth.device import generate_device
+        self.cfg, self.torch, self.moe = cfg, torch, moe
+        if weights is None:
+            self.d = generate_device(cfg, dev)
+        else:
+            xd = generate_device(cfg, dev, x_only=True)
+            self.d = weights
+            self.d = type(weights)(cfg, xd.x, xd.wr, weights.wg, weights.wu, weights.wd,
+                                   weights.sg, weights.su, weights.sd)
+        d = self.d
+        self.ws = torch.empty(moe.layer_workspace_bytes(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k,
+                                                        d.x.dtype, d.wg.dtype),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((cfg.T, cfg.H), dtype=d.x.dtype, device=dev)
+
+    def step(self):
+        d, c = self.d, self.cfg
+        self.moe.moe_layer_forward(d.x, d.wr, d.wg, d.wu, d.wd, k=c.k,
+                                   capacity_factor=c.capacity_factor, s_gate=d.sg, s_up=d.su,
+                                   s_down=d.sd, workspace=self.ws, out=self.out)
+
+    def staged_step(self, ev):
+        """The same path through the per-step entry points, with events
+        around the gate/up and down launches (ev: list of 4 events)."""
+        d, c, m = self.d, self.cfg, self.moe
+        idx, w = m.moe_router_topk(d.x, d.wr, c.k)
+        disp = m.moe_dispatch(idx, c.E, c.capacity_factor)
+        ev[0].record()
+        h = m.moe_expert_gate_up(d.x, disp["perm"], disp["offsets"], c.k, d.wg, d.wu, d.sg, d.su)
+        ev[1].record()
+        ev[2].record()
+        y = m.moe_expert_down(h, disp["offsets"], c.T, c.k, d.wd, d.sd)
+        ev[3].record()
+        m.moe_combine(y, disp["slot_row"], w)
+        return disp
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            self.step()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def stage_times(self, steps):
+        torch = self.torch
+        gu, dn = [], []
+        disp = None
+        for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            disp = self.staged_step(ev)
+            gu.append(ev)
+        torch.cuda.synchronize()
+        for ev in gu:
+            dn.append(ev[2].elapsed_time(ev[3]))
+        gu_ms = sum(ev[0].elapsed_time(ev[1]) for ev in gu) / steps
+        return gu_ms, sum(dn) / steps, disp
+
+
+def cpu_baseline(layer, n_tokens):
+    """The oracle on the first n_tokens tokens of the workload (routing and
+    dispatch over all T tokens, expert FFN and combine for the sample)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    import torch
+
+    def host_array(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+            else t.numpy()
+
+    d, c = layer.d, layer.cfg
+    log(f"cpu baseline: copying inputs to the host for {n_tokens} token(s)")
+    x = host_array(d.x)
+    wr = host_array(d.wr)
+    wg = [host_array(d.wg[e]) for e in range(c.E)]
+    wu = [host_array(d.wu[e]) for e in range(c.E)]
+    wd = [host_array(d.wd[e]) for e in range(c.E)]
+    sc = {n: (None if getattr(d, n) is None else host_array(getattr(d, n)))
+          for n in ("sg", "su", "sd")}
+    tokens = np.arange(n_tokens)
+    t0 = time.perf_counter()
+    oracle.layer_forward(x, c.act, wr, wg, wu, wd, c.wdt, k=c.k,
+                         capacity_factor=c.capacity_factor, sg=sc["sg"], su=sc["su"],
+                         sd=sc["sd"], tokens=tokens)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": (f"first {n_tokens} of the {c.T} tokens of the {c.name} workload: router, "
+                       f"top-k and dispatch over all {c.T} tokens, expert FFN and combine for the "
+                       f"sample (float64 numpy/OpenBLAS)")}
+
+
+def touched_experts(disp, E):
+    off = disp["offsets"].cpu().tolist()
+    n = [off[e + 1] - off[e] for e in range(E)]
+    return sum(1 for v in n if v > 0), n, off[E]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "skew", "capacity"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill secondary line")
+    ap.add_argument("--cpu-tokens", type=int, default=2,
+                    help="tokens in the oracle's timed sample (0 skips the CPU baseline)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import sparse_moe_transformer_top_amd as moe
+    moe.load_library()
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.workload]
+    log(f"generating {cfg.name}: T={cfg.T} H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k} "
+        f"{cfg.act}/{cfg.wdt} cf={cfg.capacity_factor}")
+    layer = Layer(cfg, dev, torch, moe)
+    torch.cuda.synchronize()
+
+    ms = layer.timed(args.steps, args.warmup)
+    log(f"{cfg.name}: {ms:.4f} ms/step")
+    gu_ms, dn_ms, disp = layer.stage_times(args.steps)
+    n_touched, n_per_e, n_kept = touched_experts(disp, cfg.E)
+    esz = {"f32": 4, "bf16": 2, "i8": 1}[cfg.wdt]
+    asz = 2 if cfg.act == "bf16" else 4
+    H, F = cfg.H, cfg.F
+    decode_like = cfg.T <= 16
+
+    # algorithmic work of the gate/up launch: every touched expert's gate and
+    # up weights read once (+ scales), the gathered x rows read, h written
+    gu_bytes = n_touched * 2 * F * H * esz + n_kept * (H + F) * asz + \
+        (n_touched * 2 * F * 4 if cfg.wdt == "i8" else 0)
+    gu_flops = 4.0 * H * F * n_kept
+    # whole layer: every touched expert's three matrices once, x read and out
+    # written, h and y_perm each written once and read once
+    layer_bytes = n_touched * 3 * F * H * esz + cfg.T * H * asz * 2 + \
+        n_kept * (H + F) * asz * 2
+    if decode_like:
+        achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profiles("gateup_decode", cfg.name),
+                "kernel": "gateup_decode_kernel<bf16>" if cfg.wdt != "i8" else
+                          "gateup_decode_kernel<i8>",
+                "algorithmic_bytes": int(gu_bytes), "mean_ms": round(gu_ms, 4)}
+    else:
+        achieved = gu_flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profiles("gateup_tiled", cfg.name),
+                "kernel": "ffn_tiled_kernel<gateup>", "algorithmic_flops": gu_flops,
+                "mean_ms": round(gu_ms, 4)}
+
+    layer_flops = 6.0 * H * F * n_kept
+    result = {
+        "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.act if cfg.wdt != "i8" else "bf16 (int8 weights)", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "T": cfg.T, "H": H, "F": F,
+                   "E": cfg.E, "k": cfg.k, "capacity_factor": cfg.capacity_factor,
+                   "weights": cfg.wdt, "experts_touched": n_touched, "rows_per_expert": n_per_e},
+        "roofline": roof,
+        "layer": {"hbm_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "TFLOPs": round(layer_flops / (ms * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                  "stages_ms": {"gate_up": round(gu_ms, 4), "down": round(dn_ms, 4)}},
+    }
+
+    if not args.no_prefill and cfg.name == "decode":
+        pcfg = synth.CONFIGS["prefill"]
+        log("prefill secondary line: same weights, T=8192 tokens")
+        pl = Layer(pcfg, dev, torch, moe, weights=layer.d)
+        pms = pl.timed(max(3, args.steps // 4), 2)
+        pgu, pdn, pdisp = pl.stage_times(max(3, args.steps // 4))
+        _, _, pk = touched_experts(pdisp, pcfg.E)
+        pflops = 6.0 * H * F * pk
+        result["prefill"] = {
+            "tokens_per_s": round(pcfg.T / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
+            "TFLOPs": round(pflops / (pms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(pflops / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "gate_up": {"ms": round(pgu, 3),
+                        "TFLOPs": round(4.0 * H * F * pk / (pgu * 1e-3) / 1e12, 1)},
+            "down": {"ms": round(pdn, 3),
+                     "TFLOPs": round(2.0 * H * F * pk / (pdn * 1e-3) / 1e12, 1)}}
+        del pl
+        torch.cuda.empty_cache()
+
+    if args.cpu_tokens > 0:
+        result["cpu_baseline"] = cpu_baseline(layer, min(args.cpu_tokens, cfg.T))
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+/*
+ * moe.h -- C ABI of the top-2 mixture-of-experts FFN layer for AMD MI355X (gfx950).
+ *
+ * The layer is the one described on the n4n.ai page "How does Grok-1 use a
+ * mixture-of-experts design?":
+ *   - a bias-free router linear from the hidden size to E expert logits
+ *     (section "The high-level architecture", GrokMoELayer; section
+ *     "Routing: top-2 without auxiliary loss", grok_router_forward);
+ *   - the top-k experts per token (k = 2 on the page) with a softmax taken
+ *     over only the k selected logits (same sections);
+ *   - dispatch of tokens to experts, with capacity-aware dropping when a
+ *     finite capacity factor is given (grok_router_forward and the paragraph
+ *     after it: capacity factor 1.25, overflow dropped in training, no drop at
+ *     inference);
+ *   - E independent SwiGLU experts w_down(silu(w_gate x) * w_up x) (section
+ *     "Expert implementation: SwiGLU at scale"; gate and up may be fused into
+ *     one product, FusedSwiGLUExpert);
+ *   - the weighted combine of each token's expert outputs back to token order
+ *     (GrokMoELayer.forward and the expert-parallel pseudocode in "Expert
+ *     parallelism vs. tensor parallelism", which scales each expert output by
+ *     its routing weight and skips experts that received no tokens).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA storage),
+ *     row-major, contiguous, owned by the caller. The library allocates and
+ *     frees nothing and keeps no state between calls apart from cached device
+ *     properties; concurrent calls on different streams are safe as long as
+ *     they do not share output or workspace buffers.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues kernels on it and returns; nothing synchronises the stream,
+ *     and no call copies data between host and device.
+ *   - Shapes: T tokens (flattened batch*seq), H hidden, F expert dim, E
+ *     experts, k experts per token. Supported: T >= 0, T*k < 2^31,
+ *     1 <= E <= 16, 1 <= k <= min(E, 4), H >= 64 and F >= 64 with
+ *     H % 64 == 0 and F % 64 == 0.
+ *   - dtypes: activations (x, h, y_perm, out) are MOE_F32 or MOE_BF16; expert
+ *     weights are MOE_F32 (with f32 activations), MOE_BF16 or MOE_I8 (with
+ *     bf16 activations). The router weight, routing weights and scales are
+ *     always float32; indices are int32.
+ *   - Weights follow nn.Linear's [out, in] layout: w_gate, w_up are [E][F][H],
+ *     w_down is [E][H][F], the router weight is [E][H]. int8 weights carry one
+ *     float32 scale per output row (s_gate, s_up [E][F], s_down [E][H]); the
+ *     effective weight is q * s.
+ *   - Errors: every argument is checked before any HIP call; a failed check
+ *     returns a non-zero status and enqueues nothing. A failed kernel launch
+ *     returns MOE_ERR_HIP. moe_last_error() gives a message for the last
+ *     failure on the calling thread. Nothing throws across the ABI.
+ *   - T == 0 is valid and returns MOE_OK; buffers whose size scales with T
+ *     may then be NULL. moe_dispatch and moe_layer_forward still write zeros
+ *     to counts/offsets (when given); nothing else is launched.
+ *   - Results are deterministic: no floating-point atomics, fixed reduction
+ *     orders; two calls with the same inputs give bitwise-equal outputs.
+ *   - NaN / Inf inputs are outside the contract.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2,        /* valid but unsupported shape / dtype combination */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2 } moe_dtype;
+
+typedef void* moe_stream_t;       /* hipStream_t */
+
+/* Name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Router + top-k + softmax (one fused kernel).
+ * Page: "Routing: top-2 without auxiliary loss" (grok_router_forward) and
+ * GrokMoELayer.forward in "The high-level architecture".
+ *
+ *   logits[t,e] = sum_h x[t,h] * w_router[e,h]      (float32 accumulation)
+ *   topk_idx[t,0..k-1]: the k largest logits in descending order; equal
+ *       logits rank the lower expert index first
+ *   topk_w[t,j] = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0)
+ *
+ * x        [T,H]  MOE_F32 or MOE_BF16 (x_dtype)
+ * w_router [E,H]  float32
+ * topk_idx [T,k]  int32 (out); topk_w [T,k] float32 (out)
+ * logits   [T,E]  float32 (out, optional: may be NULL)
+ * ------------------------------------------------------------------------ */
+moe_status moe_router_topk(const void* x, moe_dtype x_dtype, const float* w_router,
+                           int64_t T, int32_t H, int32_t E, int32_t k,
+                           int32_t* topk_idx, float* topk_w, float* logits,
+                           moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dispatch: group the T*k assignments a = t*k + j by expert, in token order,
+ * and drop assignments over capacity.
+ * Page: grok_router_forward (one-hot dispatch mask, capacity-aware dropping
+ * when the factor is finite) and the paragraph after it (capacity factor x
+ * mean load per expert; no dropping at inference).
+ *
+ *   cap = ceil(capacity_factor * (T*k) / E), evaluated in double precision;
+ *         no limit when capacity_factor <= 0 or is infinite
+ *   rank(t,j) = number of tokens t' < t that chose expert idx[t,j]
+ *   kept(t,j) = rank(t,j) < cap
+ *   counts[e]  = number of assignments to e (before the drop)      [E]
+ *   offsets[e] = sum_{e'<e} min(counts[e'], cap); offsets[E] = kept total [E+1]
+ *   perm[offsets[e] + rank] = t*k + j for kept assignments; the tail
+ *                perm[offsets[E] .. T*k-1] is set to -1                   [T*k]
+ *   slot_row[t*k+j] = offsets[e] + rank if kept, else -1                  [T*k]
+ *   dropped[t*k+j]  = 1 if not kept, else 0                      uint8    [T*k]
+ *
+ * topk_idx [T,k] int32 with entries in [0,E) and distinct per token (the
+ * router's output); out-of-range entries give undefined results.
+ * ws: device scratch of at least moe_dispatch_workspace_bytes(T,E,k) bytes.
+ * ------------------------------------------------------------------------ */
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
+moe_status moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k,
+                        float capacity_factor, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* slot_row, uint8_t* dropped,
+                        void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Expert FFN over the dispatched rows (all experts, one call).
+ * Page: "Expert implementation: SwiGLU at scale" (SwiGLUExpert and the fused
+ * gate/up form, FusedSwiGLUExpert).
+ *
+ * For every expert e and row r in [offsets[e], offsets[e+1]), with token
+ * t = perm[r] / k:
+ *   h[r,:]      = silu(x[t,:] W_gate[e]^T) * (x[t,:] W_up[e]^T)        [T*k, F]
+ *   y_perm[r,:] = h[r,:] W_down[e]^T                                 [T*k, H]
+ * silu(g) = g / (1 + exp(-g)). Products accumulate in float32; with bf16
+ * activations h is rounded to bf16 once (after silu(g)*u) and y_perm once.
+ * int8 weights are converted exactly to bf16 and each output column of the
+ * float32 accumulator is multiplied by its row scale.
+ * Rows at or past offsets[E] of h and y_perm are left unwritten.
+ *
+ * x [T,H] (act_dtype); perm [T*k] and offsets [E+1] from moe_dispatch;
+ * h [T*k,F] and y_perm [T*k,H] (act_dtype, out);
+ * s_gate/s_up/s_down must be non-NULL exactly when w_dtype == MOE_I8.
+ * Supported (act, weight) pairs: (F32,F32), (BF16,BF16), (BF16,I8).
+ * ws: device scratch of at least moe_expert_ffn_workspace_bytes(...) bytes
+ * (may be 0, then ws may be NULL).
+ * ------------------------------------------------------------------------ */
+size_t moe_expert_ffn_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                                      moe_dtype act_dtype, moe_dtype w_dtype);
+moe_status moe_expert_ffn(const void* x, moe_dtype act_dtype,
+                          const int32_t* perm, const int32_t* offsets,
+                          int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                          const void* w_gate, const void* w_up, const void* w_down,
+                          moe_dtype w_dtype,
+                          const float* s_gate, const float* s_up, const float* s_down,
+                          void* h, void* y_perm, void* ws, size_t ws_bytes,
+                          moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The two halves of moe_expert_ffn, callable on their own (moe_expert_ffn is
+ * exactly moe_expert_gate_up followed by moe_expert_down on one stream).
+ * Page: FusedSwiGLUExpert in "Expert implementation: SwiGLU at scale" (one
+ * product over the shared input for gate and up, then w_down).
+ *
+ * moe_expert_gate_up: h[r,:] = silu(x[t] W_gate[e]^T) * (x[t] W_up[e]^T),
+ *   t = perm[r] / k, for r in [offsets[e], offsets[e+1]); writes only h.
+ *   s_gate / s_up non-NULL exactly when w_dtype == MOE_I8.
+ * moe_expert_down: y_perm[r,:] = h[r,:] W_down[e]^T for the same rows.
+ *   s_down non-NULL exactly when w_dtype == MOE_I8; ws as for moe_expert_ffn.
+ * Arguments, layouts and rounding are those of moe_expert_ffn.
+ * ------------------------------------------------------------------------ */
+moe_status moe_expert_gate_up(const void* x, moe_dtype act_dtype,
+                              const int32_t* perm, const int32_t* offsets,
+                              int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                              const void* w_gate, const void* w_up, moe_dtype w_dtype,
+                              const float* s_gate, const float* s_up, void* h,
+                              moe_stream_t stream);
+moe_status moe_expert_down(const void* h, moe_dtype act_dtype, const int32_t* offsets,
+                           int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                           const void* w_down, moe_dtype w_dtype, const float* s_down,
+                           void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Weighted combine back to token order (gather form, no atomics).
+ * Page: GrokMoELayer.forward (dispatch and combine) and the expert-parallel
+ * pseudocode (each expert output scaled by its routing weight).
+ *
+ *   out[t,:] = sum_{j=0..k-1, slot_row[t*k+j] >= 0} topk_w[t,j] * y_perm[slot_row[t*k+j],:]
+ * summed in float32 in slot order j = 0, 1, ... and rounded once to act_dtype;
+ * a token whose slots were all dropped gets a zero row.
+ *
+ * y_perm [T*k,H] (act_dtype), slot_row [T*k] int32, topk_w [T,k] float32,
+ * out [T,H] (act_dtype, out).
+ * ------------------------------------------------------------------------ */
+moe_status moe_combine(const void* y_perm, const int32_t* slot_row, const float* topk_w,
+                       int64_t T, int32_t H, int32_t k, moe_dtype act_dtype, void* out,
+                       moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The whole layer: router_topk -> dispatch -> expert_ffn -> combine on one
+ * stream, with no host synchronisation. Page: GrokMoELayer.forward.
+ *
+ * out [T,H] (act_dtype, out). Optional outputs (each may be NULL):
+ *   topk_idx [T,k] int32, topk_w [T,k] float32, counts [E] int32,
+ *   offsets [E+1] int32, dropped [T*k] uint8.
+ * capacity_factor <= 0 or infinite: no capacity limit (inference).
+ * ws: device scratch of at least moe_layer_workspace_bytes(...) bytes; it
+ * holds the routing arrays, h and y_perm between the steps.
+ * ------------------------------------------------------------------------ */
+size_t moe_layer_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                                 moe_dtype act_dtype, moe_dtype w_dtype);
+moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_router,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             moe_dtype w_dtype,
+                             const float* s_gate, const float* s_up, const float* s_down,
+                             int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                             float capacity_factor, void* out,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts,
+                             int32_t* offsets, uint8_t* dropped,
+                             void* ws, size_t ws_bytes, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -187,12 +187,30 @@ def silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
+def expert_hidden(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray) -> np.ndarray:
+    """The expert's hidden activation on rows x [m,H]: silu(x Wg^T) * (x Wu^T) -> [m,F]."""
+    return silu(x64 @ wg64.T) * (x64 @ wu64.T)
+
+
 def swiglu_expert(x64: np.ndarray, wg64: np.ndarray, wu64: np.ndarray,
                   wd64: np.ndarray) -> np.ndarray:
     """One expert on rows x [m,H]: (silu(x Wg^T) * (x Wu^T)) Wd^T -> [m,H]."""
-    g = x64 @ wg64.T
-    u = x64 @ wu64.T
-    return (silu(g) * u) @ wd64.T
+    return expert_hidden(x64, wg64, wu64) @ wd64.T
+
+
+def combine(y_rows: np.ndarray, slot_row: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Weighted combine back to token order: out[t] = sum over slots j with
+    slot_row[t*k+j] >= 0 of w[t,j] * y_rows[slot_row[t*k+j]], slot 0 first;
+    zero rows for tokens whose slots were all dropped (GrokMoELayer.forward;
+    the EP pseudocode scales each expert output by the token's weight)."""
+    T, k = w.shape
+    out = np.zeros((T, y_rows.shape[1]), np.float64)
+    for t in range(T):
+        for j in range(k):
+            r = int(slot_row[t * k + j])
+            if r >= 0:
+                out[t] += float(w[t, j]) * y_rows[r].astype(np.float64)
+    return out
 
 
 # --------------------------------------------------------------------------

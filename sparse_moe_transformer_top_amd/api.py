@@ -1,0 +1,180 @@
+"""Python binding of the layer's C ABI (torch tensors in, torch tensors out).
+
+Argument marshalling only: shapes and dtypes are read off the tensors, output
+buffers are allocated with torch on the input's device, and each function
+makes exactly one call into libmoe.so on torch's current stream. Every step
+of the layer runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, MOE_I8, check
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8}
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions")
+
+
+def _cf(capacity_factor) -> float:
+    return 0.0 if capacity_factor is None else float(capacity_factor)
+
+
+def moe_router_topk(x: torch.Tensor, w_router: torch.Tensor, k: int = 2,
+                    return_logits: bool = False):
+    """(topk_idx [T,k] int32, topk_w [T,k] float32[, logits [T,E] float32])."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    _need(w_router, "w_router", torch.float32, 2)
+    T, H = x.shape
+    E = w_router.shape[0]
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
+    check(_lib.load().moe_router_topk(_p(x), _DT[x.dtype], _p(w_router), T, H, E, k, _p(idx),
+                                      _p(w), _p(logits), _stream(x.device)))
+    return (idx, w, logits) if return_logits else (idx, w)
+
+
+def moe_dispatch(topk_idx: torch.Tensor, E: int, capacity_factor: Optional[float] = None):
+    """dict(counts [E], offsets [E+1], perm [T*k], slot_row [T*k] int32, dropped [T*k] uint8)."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+               perm=torch.empty(T * k, **i32), slot_row=torch.empty(T * k, **i32),
+               dropped=torch.empty(T * k, dtype=torch.uint8, device=dev))
+    lib = _lib.load()
+    nws = lib.moe_dispatch_workspace_bytes(T, E, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    check(lib.moe_dispatch(_p(topk_idx), T, E, k, _cf(capacity_factor), _p(out["counts"]),
+                           _p(out["offsets"]), _p(out["perm"]), _p(out["slot_row"]),
+                           _p(out["dropped"]), _p(ws), nws, _stream(dev)))
+    return out
+
+
+def moe_expert_ffn(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, k: int,
+                   w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                   s_gate=None, s_up=None, s_down=None):
+    """(h [T*k,F], y_perm [T*k,H]) in x's dtype; rows past offsets[E] are unwritten."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    for n, t in (("perm", perm), ("offsets", offsets)):
+        _need(t, n, torch.int32, 1)
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, n, (torch.float32, torch.bfloat16, torch.int8), 3)
+    T, H = x.shape
+    E, F, _ = w_gate.shape
+    h = torch.empty((T * k, F), dtype=x.dtype, device=x.device)
+    y = torch.empty((T * k, H), dtype=x.dtype, device=x.device)
+    lib = _lib.load()
+    nws = lib.moe_expert_ffn_workspace_bytes(T, H, F, E, k, _DT[x.dtype], _DT[w_gate.dtype])
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    check(lib.moe_expert_ffn(_p(x), _DT[x.dtype], _p(perm), _p(offsets), T, H, F, E, k,
+                             _p(w_gate), _p(w_up), _p(w_down), _DT[w_gate.dtype], _p(s_gate),
+                             _p(s_up), _p(s_down), _p(h), _p(y), _p(ws), nws, _stream(x.device)))
+    return h, y
+
+
+def moe_expert_gate_up(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, k: int,
+                       w_gate: torch.Tensor, w_up: torch.Tensor, s_gate=None, s_up=None,
+                       h: Optional[torch.Tensor] = None):
+    """h [T*k,F] = silu(x W_gate^T) * (x W_up^T) over the dispatched rows."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    T, H = x.shape
+    E, F, _ = w_gate.shape
+    if h is None:
+        h = torch.empty((T * k, F), dtype=x.dtype, device=x.device)
+    check(_lib.load().moe_expert_gate_up(_p(x), _DT[x.dtype], _p(perm), _p(offsets), T, H, F, E,
+                                         k, _p(w_gate), _p(w_up), _DT[w_gate.dtype], _p(s_gate),
+                                         _p(s_up), _p(h), _stream(x.device)))
+    return h
+
+
+def moe_expert_down(h: torch.Tensor, offsets: torch.Tensor, T: int, k: int,
+                    w_down: torch.Tensor, s_down=None, y_perm: Optional[torch.Tensor] = None):
+    """y_perm [T*k,H] = h W_down^T over the dispatched rows."""
+    _need(h, "h", (torch.float32, torch.bfloat16), 2)
+    E, H, F = w_down.shape
+    if y_perm is None:
+        y_perm = torch.empty((T * k, H), dtype=h.dtype, device=h.device)
+    lib = _lib.load()
+    nws = lib.moe_expert_ffn_workspace_bytes(T, H, F, E, k, _DT[h.dtype], _DT[w_down.dtype])
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=h.device)
+    check(lib.moe_expert_down(_p(h), _DT[h.dtype], _p(offsets), T, H, F, E, k, _p(w_down),
+                              _DT[w_down.dtype], _p(s_down), _p(y_perm), _p(ws), nws,
+                              _stream(h.device)))
+    return y_perm
+
+
+def moe_combine(y_perm: torch.Tensor, slot_row: torch.Tensor, topk_w: torch.Tensor):
+    """out [T,H] in y_perm's dtype."""
+    _need(y_perm, "y_perm", (torch.float32, torch.bfloat16), 2)
+    _need(slot_row, "slot_row", torch.int32, 1)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    T, k = topk_w.shape
+    H = y_perm.shape[1]
+    out = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device)
+    check(_lib.load().moe_combine(_p(y_perm), _p(slot_row), _p(topk_w), T, H, k,
+                                  _DT[y_perm.dtype], _p(out), _stream(y_perm.device)))
+    return out
+
+
+def layer_workspace_bytes(T: int, H: int, F: int, E: int, k: int, act: torch.dtype,
+                          wdt: torch.dtype) -> int:
+    return _lib.load().moe_layer_workspace_bytes(T, H, F, E, k, _DT[act], _DT[wdt])
+
+
+def moe_layer_forward(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
+                      w_up: torch.Tensor, w_down: torch.Tensor, k: int = 2,
+                      capacity_factor: Optional[float] = None, s_gate=None, s_up=None,
+                      s_down=None, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, aux: bool = False):
+    """The whole layer. Returns out [T,H], or (out, dict of routing outputs) with aux=True."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    _need(w_router, "w_router", torch.float32, 2)
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, n, (torch.float32, torch.bfloat16, torch.int8), 3)
+    T, H = x.shape
+    E, F, _ = w_gate.shape
+    dev = x.device
+    nws = layer_workspace_bytes(T, H, F, E, k, x.dtype, w_gate.dtype)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    ax = None
+    if aux:
+        i32 = dict(dtype=torch.int32, device=dev)
+        ax = dict(topk_idx=torch.empty((T, k), **i32),
+                  topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                  counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                  dropped=torch.empty(T * k, dtype=torch.uint8, device=dev))
+    g = (lambda n: None if ax is None else _p(ax[n]))
+    check(_lib.load().moe_layer_forward(
+        _p(x), _DT[x.dtype], _p(w_router), _p(w_gate), _p(w_up), _p(w_down), _DT[w_gate.dtype],
+        _p(s_gate), _p(s_up), _p(s_down), T, H, F, E, k, _cf(capacity_factor), _p(out),
+        g("topk_idx"), g("topk_w"), g("counts"), g("offsets"), g("dropped"), _p(workspace),
+        workspace.numel(), _stream(dev)))
+    return (out, ax) if aux else out

@@ -1,0 +1,384 @@
+// C ABI of the top-2 MoE FFN layer: argument checks, workspace layout and
+// kernel launches. The contract of every entry point is in include/moe.h.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_size(moe_dtype d) { return d == MOE_F32 ? 4 : 2; }
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+moe_status check_shape(int64_t T, int32_t E, int32_t k) {
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %lld)", (long long)T);
+  REQUIRE(E >= 1 && k >= 1 && k <= E, MOE_ERR_INVALID_ARGUMENT,
+          "need 1 <= k <= E (got E=%d k=%d)", E, k);
+  REQUIRE(E <= 16, MOE_ERR_UNSUPPORTED, "E=%d > 16 experts is not supported", E);
+  REQUIRE(k <= 4, MOE_ERR_UNSUPPORTED, "k=%d > 4 is not supported", k);
+  REQUIRE(T * (int64_t)k < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+          "T*k=%lld does not fit int32 row indices", (long long)(T * k));
+  return ok();
+}
+
+moe_status check_dim(const char* name, int32_t v) {
+  REQUIRE(v >= 1, MOE_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %d)", name, v);
+  REQUIRE(v % 64 == 0, MOE_ERR_UNSUPPORTED, "%s=%d must be a multiple of 64", name, v);
+  return ok();
+}
+
+moe_status check_act(moe_dtype a) {
+  REQUIRE(a == MOE_F32 || a == MOE_BF16, MOE_ERR_UNSUPPORTED,
+          "activation dtype %d: only MOE_F32 and MOE_BF16 are supported", (int)a);
+  return ok();
+}
+
+moe_status check_pair(moe_dtype act, moe_dtype w) {
+  moe_status s = check_act(act);
+  if (s) return s;
+  const bool good = (act == MOE_F32 && w == MOE_F32) ||
+                    (act == MOE_BF16 && (w == MOE_BF16 || w == MOE_I8));
+  REQUIRE(good, MOE_ERR_UNSUPPORTED,
+          "unsupported (activation, weight) dtypes (%d, %d): use (F32,F32), (BF16,BF16) or "
+          "(BF16,I8)", (int)act, (int)w);
+  return ok();
+}
+
+int64_t capacity_of(int64_t T, int32_t k, int32_t E, float cf) {
+  if (!(cf > 0.0f) || std::isinf(cf)) return -1;
+  return (int64_t)std::ceil((double)cf * (double)(T * k) / (double)E);
+}
+
+struct LayerWs {
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* slot_row;
+  uint8_t* dropped;
+  void* dws;
+  void* h;
+  void* y;
+  void* fws;
+  size_t total;
+};
+
+LayerWs layer_ws_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                        moe_dtype act, moe_dtype wt) {
+  LayerWs L{};
+  const int64_t N = T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return static_cast<void*>(p);
+  };
+  L.idx = static_cast<int32_t*>(take(N * 4));
+  L.w = static_cast<float*>(take(N * 4));
+  L.counts = static_cast<int32_t*>(take(E * 4));
+  L.offsets = static_cast<int32_t*>(take((E + 1) * 4));
+  L.perm = static_cast<int32_t*>(take(N * 4));
+  L.slot_row = static_cast<int32_t*>(take(N * 4));
+  L.dropped = static_cast<uint8_t*>(take(N));
+  L.dws = take(dispatch_ws_bytes(T, E));
+  L.h = take((size_t)N * F * act_size(act));
+  L.y = take((size_t)N * H * act_size(act));
+  L.fws = take(ffn_ws_bytes(T, H, F, E, k, act == MOE_F32 ? ACT_F32 : ACT_BF16, (Wt)wt));
+  L.total = off;
+  return L;
+}
+
+// Kernel choice: float32 -> VALU tiles; bf16 with T <= kDecodeMaxT (so at
+// most kDecodeMaxT rows per expert) -> weight-streaming decode kernels;
+// otherwise the MFMA grouped GEMM tiles.
+hipError_t launch_gateup(const FfnArgs& a, moe_dtype act, moe_dtype wt, hipStream_t s) {
+  if (act == MOE_F32) return launch_gateup_f32(a, s);
+  if (a.T <= kDecodeMaxT) return launch_gateup_decode(a, (Wt)wt, s);
+  return launch_gateup_tiled(a, (Wt)wt, s);
+}
+
+hipError_t launch_down(const FfnArgs& a, moe_dtype act, moe_dtype wt, hipStream_t s) {
+  if (act == MOE_F32) return launch_down_f32(a, s);
+  if (a.T <= kDecodeMaxT) return launch_down_decode(a, (Wt)wt, s);
+  return launch_down_tiled(a, (Wt)wt, s);
+}
+
+moe_status run_ffn(const void* x, moe_dtype act, const int32_t* perm, const int32_t* offsets,
+                   int64_t T, int32_t H, int32_t F, int32_t E, int32_t k, const void* wg,
+                   const void* wu, const void* wd, moe_dtype wt, const float* sg, const float* su,
+                   const float* sd, void* h, void* y, void* ws, hipStream_t s) {
+  FfnArgs a{x, perm, offsets, T, H, F, E, k, wg, wu, wd, sg, su, sd, h, y, ws};
+  hipError_t err = launch_gateup(a, act, wt, s);
+  if (err != hipSuccess) return hip_status(err, "expert gate/up launch");
+  return hip_status(launch_down(a, act, wt, s), "expert down launch");
+}
+
+moe_status check_ffn_common(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                            moe_dtype act, moe_dtype wt) {
+  moe_status st;
+  if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)) ||
+      (st = check_pair(act, wt)))
+    return st;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_router_topk(const void* x, moe_dtype x_dtype, const float* w_router, int64_t T,
+                           int32_t H, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
+                           float* logits, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_act(x_dtype)))
+    return st;
+  if (T == 0) return ok();  // T-sized buffers may be NULL
+  REQUIRE(x && w_router && topk_idx && topk_w, MOE_ERR_INVALID_ARGUMENT,
+          "x, w_router, topk_idx and topk_w must be non-NULL");
+  REQUIRE(aligned16(x) && aligned16(w_router), MOE_ERR_INVALID_ARGUMENT,
+          "x and w_router must be 16-byte aligned");
+  return hip_status(launch_router_topk(x, x_dtype == MOE_F32 ? ACT_F32 : ACT_BF16, w_router, T, H,
+                                       E, k, topk_idx, topk_w, logits, (hipStream_t)stream),
+                    "router launch");
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+  (void)k;
+  if (T < 0 || E < 1) return 0;
+  return dispatch_ws_bytes(T, E);
+}
+
+moe_status moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k,
+                        float capacity_factor, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* slot_row, uint8_t* dropped, void* ws, size_t ws_bytes,
+                        moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_shape(T, E, k))) return st;
+  REQUIRE(counts && offsets, MOE_ERR_INVALID_ARGUMENT, "counts and offsets must be non-NULL");
+  REQUIRE(!std::isnan(capacity_factor), MOE_ERR_INVALID_ARGUMENT, "capacity_factor is NaN");
+  if (T == 0) {
+    // counts and offsets of an empty input are zeros; T-sized buffers may be NULL
+    hipError_t e = launch_fill_i32(counts, E, 0, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_fill_i32(offsets, E + 1, 0, (hipStream_t)stream);
+    return hip_status(e, "dispatch (empty input)");
+  }
+  REQUIRE(topk_idx && perm && slot_row && dropped, MOE_ERR_INVALID_ARGUMENT,
+          "topk_idx, perm, slot_row and dropped must be non-NULL");
+  const size_t need = dispatch_ws_bytes(T, E);
+  REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE_TOO_SMALL,
+          "dispatch workspace: need %zu bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+  const int64_t cap = capacity_of(T, k, E, capacity_factor);
+  return hip_status(launch_dispatch(topk_idx, T, E, k, cap, counts, offsets, perm, slot_row,
+                                    dropped, ws, (hipStream_t)stream),
+                    "dispatch launch");
+}
+
+size_t moe_expert_ffn_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                                      moe_dtype act_dtype, moe_dtype w_dtype) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1) return 0;
+  return ffn_ws_bytes(T, H, F, E, k, act_dtype == MOE_F32 ? ACT_F32 : ACT_BF16, (Wt)w_dtype);
+}
+
+moe_status moe_expert_ffn(const void* x, moe_dtype act_dtype, const int32_t* perm,
+                          const int32_t* offsets, int64_t T, int32_t H, int32_t F, int32_t E,
+                          int32_t k, const void* w_gate, const void* w_up, const void* w_down,
+                          moe_dtype w_dtype, const float* s_gate, const float* s_up,
+                          const float* s_down, void* h, void* y_perm, void* ws, size_t ws_bytes,
+                          moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)) ||
+      (st = check_pair(act_dtype, w_dtype)))
+    return st;
+  if (T == 0) return ok();  // T-sized buffers may be NULL
+  REQUIRE(x && perm && offsets && w_gate && w_up && w_down && h && y_perm,
+          MOE_ERR_INVALID_ARGUMENT,
+          "x, perm, offsets, w_gate, w_up, w_down, h and y_perm must be non-NULL");
+  const bool i8 = w_dtype == MOE_I8;
+  REQUIRE(i8 == (s_gate && s_up && s_down) && (i8 || (!s_gate && !s_up && !s_down)),
+          MOE_ERR_INVALID_ARGUMENT, "scales must be given exactly when weights are MOE_I8");
+  REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) &&
+              aligned16(h) && aligned16(y_perm),
+          MOE_ERR_INVALID_ARGUMENT, "x, weights, h and y_perm must be 16-byte aligned");
+  const size_t need = ffn_ws_bytes(T, H, F, E, k, act_dtype == MOE_F32 ? ACT_F32 : ACT_BF16,
+                                   (Wt)w_dtype);
+  REQUIRE(ws_bytes >= need && (need == 0 || ws), MOE_ERR_WORKSPACE_TOO_SMALL,
+          "expert FFN workspace: need %zu bytes, got %zu", need, ws_bytes);
+  if (T == 0) return ok();
+  return run_ffn(x, act_dtype, perm, offsets, T, H, F, E, k, w_gate, w_up, w_down, w_dtype,
+                 s_gate, s_up, s_down, h, y_perm, ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_gate_up(const void* x, moe_dtype act_dtype, const int32_t* perm,
+                              const int32_t* offsets, int64_t T, int32_t H, int32_t F, int32_t E,
+                              int32_t k, const void* w_gate, const void* w_up, moe_dtype w_dtype,
+                              const float* s_gate, const float* s_up, void* h,
+                              moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_ffn_common(T, H, F, E, k, act_dtype, w_dtype))) return st;
+  if (T == 0) return ok();  // T-sized buffers may be NULL
+  REQUIRE(x && perm && offsets && w_gate && w_up && h, MOE_ERR_INVALID_ARGUMENT,
+          "x, perm, offsets, w_gate, w_up and h must be non-NULL");
+  const bool i8 = w_dtype == MOE_I8;
+  REQUIRE(i8 == (s_gate && s_up) && (i8 || (!s_gate && !s_up)), MOE_ERR_INVALID_ARGUMENT,
+          "scales must be given exactly when weights are MOE_I8");
+  REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(h),
+          MOE_ERR_INVALID_ARGUMENT, "x, weights and h must be 16-byte aligned");
+  FfnArgs a{x, perm, offsets, T, H, F, E, k, w_gate, w_up, nullptr, s_gate, s_up, nullptr, h,
+            nullptr, nullptr};
+  return hip_status(launch_gateup(a, act_dtype, w_dtype, (hipStream_t)stream),
+                    "expert gate/up launch");
+}
+
+moe_status moe_expert_down(const void* h, moe_dtype act_dtype, const int32_t* offsets, int64_t T,
+                           int32_t H, int32_t F, int32_t E, int32_t k, const void* w_down,
+                           moe_dtype w_dtype, const float* s_down, void* y_perm, void* ws,
+                           size_t ws_bytes, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_ffn_common(T, H, F, E, k, act_dtype, w_dtype))) return st;
+  if (T == 0) return ok();  // T-sized buffers may be NULL
+  REQUIRE(h && offsets && w_down && y_perm, MOE_ERR_INVALID_ARGUMENT,
+          "h, offsets, w_down and y_perm must be non-NULL");
+  REQUIRE((w_dtype == MOE_I8) == (s_down != nullptr), MOE_ERR_INVALID_ARGUMENT,
+          "s_down must be given exactly when weights are MOE_I8");
+  REQUIRE(aligned16(h) && aligned16(w_down) && aligned16(y_perm), MOE_ERR_INVALID_ARGUMENT,
+          "h, w_down and y_perm must be 16-byte aligned");
+  const size_t need = ffn_ws_bytes(T, H, F, E, k, act_dtype == MOE_F32 ? ACT_F32 : ACT_BF16,
+                                   (Wt)w_dtype);
+  REQUIRE(ws_bytes >= need && (need == 0 || ws), MOE_ERR_WORKSPACE_TOO_SMALL,
+          "expert down workspace: need %zu bytes, got %zu", need, ws_bytes);
+  if (T == 0) return ok();
+  FfnArgs a{nullptr, nullptr, offsets, T, H, F, E, k, nullptr, nullptr, w_down, nullptr, nullptr,
+            s_down, const_cast<void*>(h), y_perm, ws};
+  return hip_status(launch_down(a, act_dtype, w_dtype, (hipStream_t)stream),
+                    "expert down launch");
+}
+
+moe_status moe_combine(const void* y_perm, const int32_t* slot_row, const float* topk_w,
+                       int64_t T, int32_t H, int32_t k, moe_dtype act_dtype, void* out,
+                       moe_stream_t stream) {
+  moe_status st;
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARGUMENT, "T must be >= 0");
+  REQUIRE(k >= 1, MOE_ERR_INVALID_ARGUMENT, "k must be >= 1");
+  REQUIRE(k <= 4, MOE_ERR_UNSUPPORTED, "k=%d > 4 is not supported", k);
+  if ((st = check_dim("H", H)) || (st = check_act(act_dtype))) return st;
+  if (T == 0) return ok();  // T-sized buffers may be NULL
+  REQUIRE(y_perm && slot_row && topk_w && out, MOE_ERR_INVALID_ARGUMENT,
+          "y_perm, slot_row, topk_w and out must be non-NULL");
+  REQUIRE(aligned16(y_perm) && aligned16(out), MOE_ERR_INVALID_ARGUMENT,
+          "y_perm and out must be 16-byte aligned");
+  return hip_status(launch_combine(y_perm, slot_row, topk_w, T, H, k,
+                                   act_dtype == MOE_F32 ? ACT_F32 : ACT_BF16, out,
+                                   (hipStream_t)stream),
+                    "combine launch");
+}
+
+size_t moe_layer_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                                 moe_dtype act_dtype, moe_dtype w_dtype) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1) return 0;
+  return layer_ws_layout(nullptr, T, H, F, E, k, act_dtype, w_dtype).total;
+}
+
+moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_router,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             moe_dtype w_dtype, const float* s_gate, const float* s_up,
+                             const float* s_down, int64_t T, int32_t H, int32_t F, int32_t E,
+                             int32_t k, float capacity_factor, void* out, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets, uint8_t* dropped,
+                             void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)) ||
+      (st = check_pair(act_dtype, w_dtype)))
+    return st;
+  REQUIRE(!std::isnan(capacity_factor), MOE_ERR_INVALID_ARGUMENT, "capacity_factor is NaN");
+  if (T == 0) {
+    // nothing to compute; the optional per-expert outputs are zeros
+    hipError_t e = hipSuccess;
+    if (counts) e = launch_fill_i32(counts, E, 0, (hipStream_t)stream);
+    if (e == hipSuccess && offsets) e = launch_fill_i32(offsets, E + 1, 0, (hipStream_t)stream);
+    return hip_status(e, "layer (empty input)");
+  }
+  REQUIRE(x && w_router && w_gate && w_up && w_down && out, MOE_ERR_INVALID_ARGUMENT,
+          "x, w_router, w_gate, w_up, w_down and out must be non-NULL");
+  const bool i8 = w_dtype == MOE_I8;
+  REQUIRE(i8 == (s_gate && s_up && s_down) && (i8 || (!s_gate && !s_up && !s_down)),
+          MOE_ERR_INVALID_ARGUMENT, "scales must be given exactly when weights are MOE_I8");
+  REQUIRE(aligned16(x) && aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) &&
+              aligned16(w_down) && aligned16(out),
+          MOE_ERR_INVALID_ARGUMENT, "x, weights and out must be 16-byte aligned");
+  REQUIRE(!std::isnan(capacity_factor), MOE_ERR_INVALID_ARGUMENT, "capacity_factor is NaN");
+  const LayerWs need = layer_ws_layout(nullptr, T, H, F, E, k, act_dtype, w_dtype);
+  REQUIRE(ws && ws_bytes >= need.total && aligned16(ws), MOE_ERR_WORKSPACE_TOO_SMALL,
+          "layer workspace: need %zu bytes (16-byte aligned), got %zu", need.total,
+          ws ? ws_bytes : (size_t)0);
+  hipStream_t s = (hipStream_t)stream;
+  LayerWs L = layer_ws_layout(static_cast<char*>(ws), T, H, F, E, k, act_dtype, w_dtype);
+  int32_t* idx = topk_idx ? topk_idx : L.idx;
+  float* w = topk_w ? topk_w : L.w;
+  int32_t* cnt = counts ? counts : L.counts;
+  int32_t* off = offsets ? offsets : L.offsets;
+  uint8_t* drp = dropped ? dropped : L.dropped;
+  const Act act = act_dtype == MOE_F32 ? ACT_F32 : ACT_BF16;
+  hipError_t e = launch_router_topk(x, act, w_router, T, H, E, k, idx, w, nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "router launch");
+  const int64_t cap = capacity_of(T, k, E, capacity_factor);
+  e = launch_dispatch(idx, T, E, k, cap, cnt, off, L.perm, L.slot_row, drp, L.dws, s);
+  if (e != hipSuccess) return hip_status(e, "dispatch launch");
+  st = run_ffn(x, act_dtype, L.perm, off, T, H, F, E, k, w_gate, w_up, w_down, w_dtype, s_gate,
+               s_up, s_down, L.h, L.y, L.fws, s);
+  if (st) return st;
+  return hip_status(launch_combine(L.y, L.slot_row, w, T, H, k, act, out, s), "combine launch");
+}
+
+}  // extern "C"

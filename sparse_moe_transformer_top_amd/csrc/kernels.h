@@ -1,0 +1,61 @@
+// Internal launcher interface between the C ABI (capi.cpp) and the kernels.
+// Launchers assume their arguments were validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Act { ACT_F32 = 0, ACT_BF16 = 1 };
+enum Wt { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2 };
+
+// router.hip
+hipError_t launch_router_topk(const void* x, Act act, const float* wr, int64_t T, int H,
+                              int E, int k, int32_t* idx, float* w, float* logits,
+                              hipStream_t s);
+
+// dispatch.hip
+size_t dispatch_ws_bytes(int64_t T, int E);
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int E, int k, int64_t cap,
+                           int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* slot_row, uint8_t* dropped, void* ws, hipStream_t s);
+
+// fills n int32 values with v (a kernel, so it is safe inside captured graphs)
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void* y_perm, const int32_t* slot_row, const float* w,
+                          int64_t T, int H, int k, Act act, void* out, hipStream_t s);
+
+// ffn_*.hip: expert FFN over dispatched rows
+struct FfnArgs {
+  const void* x;          // [T,H] act
+  const int32_t* perm;    // [T*k]
+  const int32_t* offsets; // [E+1]
+  int64_t T;
+  int H, F, E, k;
+  const void* wg;         // [E,F,H]
+  const void* wu;         // [E,F,H]
+  const void* wd;         // [E,H,F]
+  const float* sg;        // [E,F] (int8 only)
+  const float* su;        // [E,F]
+  const float* sd;        // [E,H]
+  void* h;                // [T*k,F] act
+  void* y;                // [T*k,H] act
+  void* ws;
+};
+
+// largest T for which the decode (few rows per expert) kernels are used
+constexpr int64_t kDecodeMaxT = 16;
+
+size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt);
+// gate/up product with the SwiGLU epilogue (writes h) and down product (writes y)
+hipError_t launch_gateup_f32(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down_f32(const FfnArgs& a, hipStream_t s);
+hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
+hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
+hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s);
+hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
+
+}  // namespace moe

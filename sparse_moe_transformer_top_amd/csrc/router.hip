@@ -1,0 +1,158 @@
+// Router linear + top-k + softmax over the selected logits, one fused kernel.
+//
+// n4n.ai page "How does Grok-1 use a mixture-of-experts design?": the router
+// is a bias-free linear from the hidden size to the expert logits, followed by
+// torch.topk (largest first) and a softmax over only the k selected values
+// (section "Routing: top-2 without auxiliary loss", grok_router_forward;
+// section "The high-level architecture", GrokMoELayer.forward).
+//
+// Mapping: a work-group has 4 waves, a wave owns kTokPerWave tokens. Lanes
+// split the hidden dimension into 8-element chunks (16-byte loads of bf16 x,
+// 32 bytes of the float32 router row per expert); each router chunk is loaded
+// once per wave and reused for all the wave's tokens. Partial dot products are
+// reduced across the 64 lanes with an xor butterfly (fixed order, identical
+// result on every lane), so logits are deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTokPerWave = 4;
+constexpr int kWaves = 4;
+
+template <int ACT>
+MOE_DEV void load_x8(const void* xv, int64_t t, int H, int h0, float (&xo)[8]) {
+  if (ACT == ACT_BF16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(xv) + t * H + h0);
+    xo[0] = bf16lo(v.x); xo[1] = bf16hi(v.x); xo[2] = bf16lo(v.y); xo[3] = bf16hi(v.y);
+    xo[4] = bf16lo(v.z); xo[5] = bf16hi(v.z); xo[6] = bf16lo(v.w); xo[7] = bf16hi(v.w);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + t * H + h0);
+    const float4 a = p[0], b = p[1];
+    xo[0] = a.x; xo[1] = a.y; xo[2] = a.z; xo[3] = a.w;
+    xo[4] = b.x; xo[5] = b.y; xo[6] = b.z; xo[7] = b.w;
+  }
+}
+
+// Select the k largest of l[0..E) (descending; equal values: lower index
+// first) and write indices, softmax weights and optionally the logits.
+template <int EC>
+MOE_DEV void select_topk(const float (&l)[EC], int E, int k, int64_t t, int32_t* idx,
+                         float* w, float* logits) {
+  uint32_t taken = 0;
+  int si[4] = {0, 0, 0, 0};
+  float sv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j < k) {
+      float best = 0.f;
+      int bi = -1;
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        const bool ok = e < E && !((taken >> e) & 1u);
+        if (ok && (bi < 0 || l[e] > best)) { best = l[e]; bi = e; }
+      }
+      taken |= 1u << bi;
+      si[j] = bi;
+      sv[j] = best;
+    }
+  }
+  float z[4], zs = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    z[j] = j < k ? expf(sv[j] - sv[0]) : 0.f;
+    zs += z[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j < k) {
+      idx[t * k + j] = si[j];
+      w[t * k + j] = z[j] / zs;
+    }
+  }
+  if (logits) {
+#pragma unroll
+    for (int e = 0; e < EC; ++e)
+      if (e < E) logits[t * E + e] = l[e];
+  }
+}
+
+template <int EC, int ACT>
+__global__ __launch_bounds__(kWaves * 64) void router_topk_kernel(
+    const void* __restrict__ x, const float* __restrict__ wr, int64_t T, int H, int E, int k,
+    int32_t* __restrict__ idx, float* __restrict__ w, float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = ((int64_t)blockIdx.x * kWaves + wave) * kTokPerWave;
+  if (t0 >= T) return;
+
+  float acc[kTokPerWave][EC];
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i)
+#pragma unroll
+    for (int e = 0; e < EC; ++e) acc[i][e] = 0.f;
+
+  for (int h0 = lane * 8; h0 < H; h0 += 64 * 8) {
+    float wv[EC][8];
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      if (e < E) {
+        const float4* p = reinterpret_cast<const float4*>(wr + (int64_t)e * H + h0);
+        const float4 a = p[0], b = p[1];
+        wv[e][0] = a.x; wv[e][1] = a.y; wv[e][2] = a.z; wv[e][3] = a.w;
+        wv[e][4] = b.x; wv[e][5] = b.y; wv[e][6] = b.z; wv[e][7] = b.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[e][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTokPerWave; ++tt) {
+      const int64_t t = t0 + tt;
+      if (t < T) {
+        float xv[8];
+        load_x8<ACT>(x, t, H, h0, xv);
+#pragma unroll
+        for (int e = 0; e < EC; ++e)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[tt][e] = fmaf(xv[i], wv[e][i], acc[tt][e]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < kTokPerWave; ++tt)
+#pragma unroll
+    for (int e = 0; e < EC; ++e) acc[tt][e] = wave_sum_xor(acc[tt][e]);
+
+#pragma unroll
+  for (int tt = 0; tt < kTokPerWave; ++tt) {
+    if (lane == tt && t0 + tt < T) select_topk<EC>(acc[tt], E, k, t0 + tt, idx, w, logits);
+  }
+}
+
+template <int EC>
+hipError_t launch_ec(const void* x, Act act, const float* wr, int64_t T, int H, int E, int k,
+                     int32_t* idx, float* w, float* logits, hipStream_t s) {
+  const int64_t per_block = (int64_t)kWaves * kTokPerWave;
+  const dim3 grid((unsigned)((T + per_block - 1) / per_block));
+  if (act == ACT_BF16)
+    hipLaunchKernelGGL((router_topk_kernel<EC, ACT_BF16>), grid, dim3(kWaves * 64), 0, s, x, wr,
+                       T, H, E, k, idx, w, logits);
+  else
+    hipLaunchKernelGGL((router_topk_kernel<EC, ACT_F32>), grid, dim3(kWaves * 64), 0, s, x, wr,
+                       T, H, E, k, idx, w, logits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router_topk(const void* x, Act act, const float* wr, int64_t T, int H, int E,
+                              int k, int32_t* idx, float* w, float* logits, hipStream_t s) {
+  if (E <= 8) return launch_ec<8>(x, act, wr, T, H, E, k, idx, w, logits, s);
+  return launch_ec<16>(x, act, wr, T, H, E, k, idx, w, logits, s);
+}
+
+}  // namespace moe

@@ -48,7 +48,7 @@ class LayerConfig:
 # so the magnitudes are calibrated (oracle/calibrate_skew.py) to put roughly
 # 50% and 25% of the top-1 picks on experts 0 and 1 at each token count.
 SKEW_T4096 = (1.8, 1.4)
-SKEW_T16384 = (6.0, 5.4)
+SKEW_T16384 = (8.0, 7.4)
 
 CONFIGS = {
     "tiny": LayerConfig(
@@ -81,6 +81,10 @@ PARITY_CONFIGS = {
     "p_cap_i8": LayerConfig("p_cap_i8", T=260, H=256, F=512, capacity_factor=1.25,
                             wdt="i8", skew=(2.5, 2.0), seed=8),
     "p_skew": LayerConfig("p_skew", T=640, H=512, F=512, skew=(1.8, 1.4), seed=9),
+    # column counts that are not multiples of the GEMM tile widths
+    "p_bf16_tail": LayerConfig("p_bf16_tail", T=150, H=320, F=448, seed=10),
+    "p_i8_dec": LayerConfig("p_i8_dec", T=9, H=512, F=1024, wdt="i8", seed=11),
+    "p_dec1": LayerConfig("p_dec1", T=1, H=384, F=640, seed=12),
 }
 
 

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: libmoe.so loads, exports every function that
+include/moe.h declares, and rejects bad arguments before any HIP call."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+from sparse_moe_transformer_top_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INV, UNS, WS, HIP = 0, 1, 2, 3, 4
+F32, BF16, I8 = 0, 1, 2
+P = 0x10000           # fake, 16-byte aligned device address: never dereferenced
+MIS = 0x10008         # misaligned fake address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert [lib.moe_status_string(i).decode() for i in range(5)] == [
+        "MOE_OK", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
+        "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_HIP"]
+
+
+def router(lib, x=P, xdt=BF16, wr=P, T=8, H=128, E=8, k=2, idx=P, w=P):
+    return lib.moe_router_topk(x, xdt, wr, T, H, E, k, idx, w, None, None)
+
+
+def test_router_argument_errors(lib):
+    assert router(lib, x=None) == INV
+    assert router(lib, idx=None) == INV
+    assert router(lib, T=-1) == INV
+    assert router(lib, k=0) == INV
+    assert router(lib, k=9) == INV          # k > E
+    assert router(lib, E=17, k=2) == UNS
+    assert router(lib, k=5, E=8) == UNS
+    assert router(lib, H=100) == UNS
+    assert router(lib, H=0) == INV
+    assert router(lib, xdt=I8) == UNS
+    assert router(lib, x=MIS) == INV
+    assert "aligned" in lib.moe_last_error().decode()
+    assert router(lib, T=2 ** 31) == UNS     # T*k overflows int32 rows
+    assert router(lib, T=0) == OK            # empty input: nothing launched
+
+
+def dispatch(lib, idx=P, T=8, E=8, k=2, cf=0.0, ws=P, nws=None, outs=(P, P, P, P, P)):
+    nws = lib.moe_dispatch_workspace_bytes(T, E, k) if nws is None else nws
+    return lib.moe_dispatch(idx, T, E, k, cf, *outs, ws, nws, None)
+
+
+def test_dispatch_argument_errors(lib):
+    assert dispatch(lib, idx=None) == INV
+    assert dispatch(lib, outs=(P, P, None, P, P)) == INV
+    assert dispatch(lib, cf=math.nan) == INV
+    assert dispatch(lib, nws=0) == WS
+    assert dispatch(lib, ws=None) == WS
+    assert dispatch(lib, k=3, E=2) == INV
+    assert lib.moe_dispatch_workspace_bytes(5000, 8, 2) >= 5 * 8 * 4
+
+
+def ffn(lib, act=BF16, wdt=BF16, T=32, H=128, F=256, E=8, k=2, scales=(None, None, None),
+        ptrs=None, ws=None, nws=0):
+    p = dict(x=P, perm=P, off=P, wg=P, wu=P, wd=P, h=P, y=P)
+    p.update(ptrs or {})
+    return lib.moe_expert_ffn(p["x"], act, p["perm"], p["off"], T, H, F, E, k, p["wg"], p["wu"],
+                              p["wd"], wdt, *scales, p["h"], p["y"], ws, nws, None)
+
+
+def test_expert_ffn_argument_errors(lib):
+    assert ffn(lib, ptrs=dict(h=None)) == INV
+    assert ffn(lib, wdt=I8) == INV                          # int8 without scales
+    assert ffn(lib, scales=(P, P, P)) == INV                # scales with bf16 weights
+    assert ffn(lib, act=F32, wdt=BF16) == UNS
+    assert ffn(lib, act=F32, wdt=I8, scales=(P, P, P)) == UNS
+    assert ffn(lib, act=I8, wdt=I8, scales=(P, P, P)) == UNS
+    assert ffn(lib, F=100) == UNS
+    assert ffn(lib, ptrs=dict(wd=MIS)) == INV
+    assert ffn(lib, T=0) == OK
+
+
+def test_stage_entry_points_argument_errors(lib):
+    gu = lambda **kw: lib.moe_expert_gate_up(
+        kw.get("x", P), BF16, P, P, 32, 128, 256, 8, 2, P, P, kw.get("wdt", BF16),
+        kw.get("sg"), kw.get("su"), kw.get("h", P), None)
+    assert gu(h=None) == INV
+    assert gu(wdt=I8) == INV
+    assert gu(wdt=I8, sg=P) == INV
+    assert gu(x=MIS) == INV
+    dn = lambda **kw: lib.moe_expert_down(
+        kw.get("h", P), BF16, P, 32, 128, kw.get("F", 256), 8, 2, P, kw.get("wdt", BF16),
+        kw.get("sd"), P, None, 0, None)
+    assert dn(h=None) == INV
+    assert dn(wdt=I8) == INV
+    assert dn(sd=P) == INV
+    assert dn(F=200) == UNS
+
+
+def test_combine_argument_errors(lib):
+    assert lib.moe_combine(None, P, P, 8, 128, 2, BF16, P, None) == INV
+    assert lib.moe_combine(P, P, P, 8, 128, 0, BF16, P, None) == INV
+    assert lib.moe_combine(P, P, P, 8, 96, 2, BF16, P, None) == UNS
+    assert lib.moe_combine(P, P, P, 8, 128, 2, I8, P, None) == UNS
+    assert lib.moe_combine(P, P, P, 0, 128, 2, BF16, P, None) == OK
+
+
+def layer(lib, T=32, H=128, F=256, E=8, k=2, act=BF16, wdt=BF16, cf=0.0, ws=P, nws=None,
+          scales=(None, None, None), out=P):
+    nws = lib.moe_layer_workspace_bytes(T, H, F, E, k, act, wdt) if nws is None else nws
+    return lib.moe_layer_forward(P, act, P, P, P, P, wdt, *scales, T, H, F, E, k, cf, out,
+                                 None, None, None, None, None, ws, nws, None)
+
+
+def test_layer_argument_errors(lib):
+    assert layer(lib, out=None) == INV
+    assert layer(lib, nws=16) == WS
+    assert layer(lib, ws=None) == WS
+    assert layer(lib, ws=MIS) == WS
+    assert layer(lib, cf=math.nan) == INV
+    assert layer(lib, act=F32, wdt=I8, scales=(P, P, P)) == UNS
+    assert layer(lib, k=3, E=2) == INV
+
+
+def test_workspace_sizes(lib):
+    T, H, F, E, k = 8192, 6144, 32768, 8, 2
+    n = lib.moe_layer_workspace_bytes(T, H, F, E, k, BF16, BF16)
+    # h [T*k, F] and y_perm [T*k, H] in bf16 dominate
+    assert n >= T * k * (F + H) * 2
+    assert n < T * k * (F + H) * 2 + 64 * 2 ** 20
+    assert lib.moe_layer_workspace_bytes(T, H, F, E, k, F32, F32) > n
+    assert lib.moe_layer_workspace_bytes(0, H, F, E, k, BF16, BF16) > 0
+    assert lib.moe_expert_ffn_workspace_bytes(T, H, F, E, k, BF16, BF16) >= 0

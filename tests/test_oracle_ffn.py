@@ -153,3 +153,32 @@ def test_widen_int8_and_bf16():
     t = torch.randn(1000).to(torch.bfloat16)
     bits = t.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle.widen(bits, "bf16"), t.to(torch.float64).numpy())
+
+
+def test_combine_and_hidden_agree_with_layer():
+    # expert_hidden @ Wd^T per dispatched row, then combine == layer_forward
+    cfg = synth.get_config("p_cap")
+    inp = synth.generate_host(cfg)
+    res = _layer(inp, cfg)
+    x = oracle.widen(inp.x, cfg.act)
+    n_rows = int(res.disp.offsets[-1])
+    y = np.zeros((cfg.T * cfg.k, cfg.H))
+    for e in range(cfg.E):
+        rows = np.arange(res.disp.offsets[e], res.disp.offsets[e + 1])
+        if rows.size == 0:
+            continue
+        tok = res.disp.perm[rows] // cfg.k
+        h = oracle.expert_hidden(x[tok], oracle.widen(inp.wg[e], cfg.wdt),
+                                 oracle.widen(inp.wu[e], cfg.wdt))
+        y[rows] = h @ oracle.widen(inp.wd[e], cfg.wdt).T
+    out = oracle.combine(y[:n_rows], res.disp.slot_row, res.routing.w)
+    assert np.max(np.abs(out - res.out)) < 1e-12 * np.abs(res.out).max()
+
+
+def test_combine_hand_case():
+    # two tokens, k = 2: token 0 keeps rows 1 and 0; token 1 drops slot 1
+    y = np.array([[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]])
+    slot_row = np.array([1, 0, 2, -1])
+    w = np.array([[0.75, 0.25], [0.6, 0.4]])
+    out = oracle.combine(y, slot_row, w)
+    assert out.tolist() == [[7.75, 15.5], [60.0, 120.0]]
