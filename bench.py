@@ -189,8 +189,11 @@ def main():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "capacity"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill secondary line")
-    ap.add_argument("--cpu-tokens", type=int, default=2,
+    ap.add_argument("--cpu-tokens", type=int, default=8,
                     help="tokens in the oracle's timed sample (0 skips the CPU baseline)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (float32 negate: reads "
+                         "and writes MIB MiB per launch) 3 times, to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -198,6 +201,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20 // 4
+        a = torch.randn(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n * 4}))
+        return
     import synth
     import sparse_moe_transformer_top_amd as moe
     moe.load_library()

@@ -7,48 +7,50 @@
 // expert the layer's cost is reading the experts' weights once).
 //
 // With at most 16 rows per expert every weight element is used by <= 16 rows,
-// so the kernels are bound by HBM: the goal is to stream each touched
-// expert's weights exactly once at full bandwidth, and nothing else. A
-// work-group owns 16 weight rows of one expert (gate and up rows of the same
-// 16 output columns for kernel 1, 16 down rows for kernel 2) and splits k
-// across its 4 waves; each lane keeps kInFlight independent 16-byte weight
-// loads outstanding. The products run on v_mfma_f32_16x16x32_bf16 with the
-// expert's rows as the 16-row A operand (rows past n_e are zero). The 4
-// waves' partial sums are added in wave order through LDS. int8 weights are
-// loaded 16 per lane (64 k per step) and converted exactly to bf16; their
-// row scales multiply the float32 sums.
+// so these kernels are bound by HBM: the goal is to stream each touched
+// expert's weights exactly once at full bandwidth. A work-group owns 16 weight
+// rows of one expert (the gate and up rows of the same 16 output columns for
+// kernel 1; 16 down rows and one k split for kernel 2); its waves take the
+// row's k steps round-robin, so at any time the waves of a work-group read
+// neighbouring 64-byte pieces of the same 128-byte lines, and each lane keeps
+// kInFlight 16-byte weight loads outstanding. (Measured on MI355X at the
+// Grok-1 shape: interleaved steps beat one contiguous k range per wave, and
+// nontemporal loads lose about a quarter of the bandwidth.) The products run
+// on v_mfma_f32_16x16x32_bf16 with the expert's rows as the 16-row A operand
+// (rows past n_e are zero). The waves' partial sums are added in wave order
+// through LDS. int8 weights are loaded 16 per lane (64 k per step) and
+// converted exactly to bf16; their row scales multiply the float32 sums.
+//
+// The down projection is split over kDownSplit k ranges so that a work unit
+// (16 rows x F/kDownSplit) is small against the whole launch and the last
+// round of work-groups does not leave most of the GPU idle; the float32
+// partials are summed in split order by a small reduce kernel.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kInFlight = 8;
+constexpr int kWavesGateUp = 16;
+constexpr int kWavesDown = 8;
+constexpr int kInFlight = 4;
+constexpr int kDownSplit = 8;
 
-typedef float f32x4v __attribute__((ext_vector_type(4)));
+MOE_DEV u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-MOE_DEV uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// One k step of one lane: A (activation) operand(s) and B (weight) operand(s).
-// bf16 weights: 32 k per step, one A and one B operand.
-// int8 weights: 64 k per step, two A operands (32 contiguous bytes of the
-// row), one 16-byte int8 load split into two B operands.
 template <int WT>
 struct Step {
-  static constexpr int K = WT == WT_I8 ? 64 : 32;
+  static constexpr int K = WT == WT_I8 ? 64 : 32;  // k per MFMA step of one lane group
+  static constexpr int ESZ = WT == WT_I8 ? 1 : 2;  // weight element bytes
 };
 
 template <int WT, int NB>
-MOE_DEV void mfma_step(const uint4 (&av)[2], const uint4 (&bv)[NB], f32x4v (&acc)[NB]) {
+MOE_DEV void mfma_step(const u32x4 (&av)[2], const u32x4 (&bv)[NB], f32x4 (&acc)[NB]) {
   if (WT == WT_I8) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      uint4 lo, hi;
-      i8x4_to_bf16x4(bv[b].x, lo.x, lo.y);
-      i8x4_to_bf16x4(bv[b].y, lo.z, lo.w);
-      i8x4_to_bf16x4(bv[b].z, hi.x, hi.y);
-      i8x4_to_bf16x4(bv[b].w, hi.z, hi.w);
+      const u32x4 lo = i8x8_to_bf16x8(bv[b].x, bv[b].y);
+      const u32x4 hi = i8x8_to_bf16x8(bv[b].z, bv[b].w);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[0]), as_bf16x8(lo), acc[b], 0,
                                                        0, 0);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[1]), as_bf16x8(hi), acc[b], 0,
@@ -62,40 +64,47 @@ MOE_DEV void mfma_step(const uint4 (&av)[2], const uint4 (&bv)[NB], f32x4v (&acc
   }
 }
 
-// Stream NB weight matrices' rows [n0, n0+16) (row length K) against the
-// A rows arow (nullptr for a zero row). Returns this wave's partial sums.
-template <int WT, int NB>
-MOE_DEV void stream_rows(const uint16_t* arow, const char* const (&wrow)[NB], int K, int wave,
-                         int g, f32x4v (&acc)[NB]) {
+// Accumulate this wave's steps of [s_begin, s_end) (in units of Step<WT>::K;
+// the wave takes steps s_begin + wave, + W, + 2W, ...) of NB weight rows
+// against the activation row arow (nullptr: zero row). Lane group g
+// (lane / 16) covers 8 (bf16) or 16 (int8) consecutive k of each step.
+template <int WT, int NB, int W>
+MOE_DEV void stream_steps(const uint16_t* arow, const char* const (&wrow)[NB], int s_begin,
+                          int s_end, int wave, int g, f32x4 (&acc)[NB]) {
   constexpr int KS = Step<WT>::K;
-  constexpr int ESZ = WT == WT_I8 ? 1 : 2;
-  const int nsteps = K / KS;
-  for (int s0 = wave; s0 < nsteps; s0 += kWaves * kInFlight) {
-    uint4 bv[kInFlight][NB];
-    uint4 av[kInFlight][2];
+  constexpr int ESZ = Step<WT>::ESZ;
+  const int kl = WT == WT_I8 ? 16 * g : 8 * g;
+  for (int s0 = s_begin + wave; s0 < s_end; s0 += W * kInFlight) {
+    u32x4 bv[kInFlight][NB];
+    u32x4 av[kInFlight][2];
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
-      const int s = s0 + kWaves * u;
-      if (s < nsteps) {
-        const int k0 = s * KS;
-        const int kl = WT == WT_I8 ? 16 * g : 8 * g;  // this lane's first k within the step
+      if (s0 + W * u < s_end) {
+        const int k = (s0 + W * u) * KS + kl;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) bv[u][b] = ldg16(wrow[b] + (int64_t)(k0 + kl) * ESZ);
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        av[u][0] = arow ? ldg16(arow + k0 + kl) : z;
-        av[u][1] = (WT == WT_I8 && arow) ? ldg16(arow + k0 + kl + 8) : z;
+        for (int b = 0; b < NB; ++b) bv[u][b] = ldg16(wrow[b] + (int64_t)k * ESZ);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        av[u][0] = arow ? ldg16(arow + k) : z;
+        av[u][1] = (WT == WT_I8 && arow) ? ldg16(arow + k + 8) : z;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u) {
-      if (s0 + kWaves * u < nsteps) mfma_step<WT, NB>(av[u], bv[u], acc);
-    }
+    for (int u = 0; u < kInFlight; ++u)
+      if (s0 + W * u < s_end) mfma_step<WT, NB>(av[u], bv[u], acc);
   }
+}
+
+// contiguous share [b, e) of n steps for part p of parts
+MOE_DEV void split_range(int n, int parts, int p, int& b, int& e) {
+  const int q = (n + parts - 1) / parts;
+  b = min(n, p * q);
+  e = min(n, b + q);
 }
 
 // Kernel 1: h = silu(x W_gate^T) * (x W_up^T) for <= 16 rows per expert.
 template <int WT>
-__global__ __launch_bounds__(kWaves * 64) void gateup_decode_kernel(FfnArgs a) {
+__global__ __launch_bounds__(kWavesGateUp * 64) void gateup_decode_kernel(FfnArgs a) {
+  constexpr int kWaves = kWavesGateUp;
   __shared__ float red[kWaves][2][4][64];
   const int nt_per_e = (a.F + 15) / 16;
   const int e = blockIdx.x / nt_per_e;
@@ -108,14 +117,13 @@ __global__ __launch_bounds__(kWaves * 64) void gateup_decode_kernel(FfnArgs a) {
   const uint16_t* arow = nullptr;
   if (i < ne) arow = static_cast<const uint16_t*>(a.x) + (int64_t)(a.perm[r0 + i] / a.k) * a.H;
   const int n = min(n0 + i, a.F - 1);
-  constexpr int ESZ = WT == WT_I8 ? 1 : 2;
-  const int64_t roff = ((int64_t)e * a.F + n) * a.H * ESZ;
+  const int64_t roff = ((int64_t)e * a.F + n) * a.H * Step<WT>::ESZ;
   const char* const wrow[2] = {static_cast<const char*>(a.wg) + roff,
                                static_cast<const char*>(a.wu) + roff};
-  f32x4v acc[2];
-  acc[0] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2];
+  acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   acc[1] = acc[0];
-  stream_rows<WT, 2>(arow, wrow, a.H, wave, g, acc);
+  stream_steps<WT, 2, kWaves>(arow, wrow, 0, a.H / Step<WT>::K, wave, g, acc);
 
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -145,13 +153,17 @@ __global__ __launch_bounds__(kWaves * 64) void gateup_decode_kernel(FfnArgs a) {
   }
 }
 
-// Kernel 2: y = h W_down^T for <= 16 rows per expert.
+// Kernel 2: float32 partial sums of y = h W_down^T over one k split, for
+// <= 16 rows per expert: part[split][row][H].
 template <int WT>
-__global__ __launch_bounds__(kWaves * 64) void down_decode_kernel(FfnArgs a) {
+__global__ __launch_bounds__(kWavesDown * 64) void down_decode_kernel(FfnArgs a) {
+  constexpr int kWaves = kWavesDown;
   __shared__ float red[kWaves][4][64];
   const int nt_per_e = (a.H + 15) / 16;
-  const int e = blockIdx.x / nt_per_e;
-  const int n0 = (blockIdx.x % nt_per_e) * 16;
+  const int split = blockIdx.x % kDownSplit;
+  const int tile = blockIdx.x / kDownSplit;
+  const int e = tile / nt_per_e;
+  const int n0 = (tile % nt_per_e) * 16;
   const int r0 = a.offsets[e];
   const int ne = a.offsets[e + 1] - r0;
   if (ne <= 0) return;
@@ -160,12 +172,13 @@ __global__ __launch_bounds__(kWaves * 64) void down_decode_kernel(FfnArgs a) {
   const uint16_t* arow = i < ne ? static_cast<const uint16_t*>(a.h) + (int64_t)(r0 + i) * a.F
                                 : nullptr;
   const int n = min(n0 + i, a.H - 1);
-  constexpr int ESZ = WT == WT_I8 ? 1 : 2;
   const char* const wrow[1] = {static_cast<const char*>(a.wd) +
-                               ((int64_t)e * a.H + n) * a.F * ESZ};
-  f32x4v acc[1];
-  acc[0] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  stream_rows<WT, 1>(arow, wrow, a.F, wave, g, acc);
+                               ((int64_t)e * a.H + n) * a.F * Step<WT>::ESZ};
+  f32x4 acc[1];
+  acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int kb, ke;
+  split_range(a.F / Step<WT>::K, kDownSplit, split, kb, ke);
+  stream_steps<WT, 1, kWaves>(arow, wrow, kb, ke, wave, g, acc);
 
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[0][v];
@@ -173,6 +186,7 @@ __global__ __launch_bounds__(kWaves * 64) void down_decode_kernel(FfnArgs a) {
   if (wave != 0) return;
   const int col = n0 + i;
   if (col >= a.H) return;
+  float* part = static_cast<float*>(a.ws) + (int64_t)split * a.T * a.k * a.H;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int row = 4 * g + v;
@@ -181,27 +195,57 @@ __global__ __launch_bounds__(kWaves * 64) void down_decode_kernel(FfnArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) ys += red[w][v][lane];
     if (WT == WT_I8) ys *= a.sd[(int64_t)e * a.H + col];
-    static_cast<uint16_t*>(a.y)[(int64_t)(r0 + row) * a.H + col] = f32_to_bf16_bits(ys);
+    part[(int64_t)(r0 + row) * a.H + col] = ys;
   }
+}
+
+// y[r, :] = bf16(sum over splits of part[split][r][:]) for r < offsets[E].
+__global__ __launch_bounds__(256) void down_reduce_kernel(FfnArgs a) {
+  const int chunks = a.H / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = gid / chunks;
+  if (r >= a.offsets[a.E]) return;
+  const int c = (int)(gid - r * chunks) * 4;
+  const float* part = static_cast<const float*>(a.ws);
+  const int64_t stride = a.T * a.k * a.H;
+  float4 s = *reinterpret_cast<const float4*>(part + r * a.H + c);
+#pragma unroll
+  for (int p = 1; p < kDownSplit; ++p) {
+    const float4 v = *reinterpret_cast<const float4*>(part + p * stride + r * a.H + c);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  uint2 o;
+  o.x = pack_bf16x2(s.x, s.y);
+  o.y = pack_bf16x2(s.z, s.w);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + r * a.H + c) = o;
 }
 
 }  // namespace
 
+size_t decode_ws_bytes(int64_t T, int H, int k) {
+  return (size_t)kDownSplit * T * k * H * sizeof(float);
+}
+
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
   const dim3 grid((unsigned)(a.E * ((a.F + 15) / 16)));
   if (wt == WT_I8)
-    hipLaunchKernelGGL(gateup_decode_kernel<WT_I8>, grid, dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(gateup_decode_kernel<WT_I8>, grid, dim3(kWavesGateUp * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(gateup_decode_kernel<WT_BF16>, grid, dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(gateup_decode_kernel<WT_BF16>, grid, dim3(kWavesGateUp * 64), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
-  const dim3 grid((unsigned)(a.E * ((a.H + 15) / 16)));
+  const dim3 grid((unsigned)(a.E * ((a.H + 15) / 16) * kDownSplit));
   if (wt == WT_I8)
-    hipLaunchKernelGGL(down_decode_kernel<WT_I8>, grid, dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(down_decode_kernel<WT_I8>, grid, dim3(kWavesDown * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(down_decode_kernel<WT_BF16>, grid, dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(down_decode_kernel<WT_BF16>, grid, dim3(kWavesDown * 64), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t items = a.T * a.k * (a.H / 4);
+  hipLaunchKernelGGL(down_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 

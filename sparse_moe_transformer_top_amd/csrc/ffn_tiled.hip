@@ -203,7 +203,11 @@ hipError_t launch_one(const FfnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t ffn_ws_bytes(int64_t, int, int, int, int, Act, Wt) { return 0; }
+size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt) {
+  (void)F; (void)E; (void)wt;
+  // the decode path keeps float32 split-k partials of the down projection
+  return (act == ACT_BF16 && T <= kDecodeMaxT) ? decode_ws_bytes(T, H, k) : 0;
+}
 
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
   return wt == WT_I8 ? launch_one<true, WT_I8>(a, s) : launch_one<true, WT_BF16>(a, s);

@@ -55,6 +55,7 @@ hipError_t launch_gateup_f32(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_f32(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
+size_t decode_ws_bytes(int64_t T, int H, int k);
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 
