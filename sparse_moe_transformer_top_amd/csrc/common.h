@@ -29,18 +29,19 @@ MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
 // library's; for g -> -inf the quotient goes to -0, for g -> +inf to g * u.
 MOE_DEV float swiglu(float g, float u) { return g * u / (1.0f + __expf(-g)); }
 
-// Four int8 values packed in a word -> two words of packed bf16 (exact:
-// |q| <= 127 fits the 8-bit bf16 significand). The signed byte is biased to
-// unsigned (xor 0x80), converted with v_cvt_f32_ubyteN, and 128 subtracted.
+// Four int8 values packed in a word -> two words of packed bf16 (exact: an
+// int8 has at most 8 significant bits, which the bf16 significand holds, so
+// the high half of the float32 is the bf16 value). Each byte converts with
+// one sign-extending v_cvt_f32_i32 (SDWA byte select); v_perm_b32 packs the
+// high halves of two floats into one word.
+MOE_DEV uint32_t pack_hi_halves(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
 MOE_DEV void i8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32_t& hi) {
-  uint32_t u = q ^ 0x80808080u;
-  float f0 = (float)(u & 0xffu) - 128.0f;
-  float f1 = (float)((u >> 8) & 0xffu) - 128.0f;
-  float f2 = (float)((u >> 16) & 0xffu) - 128.0f;
-  float f3 = (float)(u >> 24) - 128.0f;
-  // exact values: taking the high halves is exact
-  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  const float f0 = (float)(int8_t)q, f1 = (float)(int8_t)(q >> 8);
+  const float f2 = (float)(int8_t)(q >> 16), f3 = (float)((int32_t)q >> 24);
+  lo = pack_hi_halves(f0, f1);
+  hi = pack_hi_halves(f2, f3);
 }
 
 // Eight int8 values (two words) -> eight bf16 (one 16-byte vector), exact.

@@ -12,7 +12,7 @@
 // [n][k]), so each 16-byte load holds 8 consecutive k of one row, which is the
 // per-lane operand of v_mfma_f32_32x32x16_bf16.
 //
-// bf16 weights (ffn_mfma_kernel): a work-group of 8 waves computes a tile of
+// A work-group of 8 waves computes a tile of
 // 256 activation rows x 256 weight rows (gate 128 + up 128, or 256 down
 // columns); waves form a 4 x 2 grid, each wave 64 rows x 4 weight sub-tiles
 // of 32 (8 MFMA accumulators of 32x32, two waves per SIMD). k advances in
@@ -25,9 +25,9 @@
 // each MFMA. LDS rows use a 16-byte-chunk XOR swizzle so the 32 lanes reading
 // one chunk column of 32 consecutive rows hit distinct banks.
 //
-// int8 weights (ffn_tiled_kernel): 128 x 256 tiles of 4 waves, staged through
-// registers so that the weights can be converted exactly to bf16 on their way
-// into LDS; per-row scales multiply the float32 accumulators in the epilogue.
+// int8 weights travel to LDS as int8 (half the bytes of the B tile) and are
+// converted exactly to bf16 when each wave loads its MFMA operands; their
+// per-row scales multiply the float32 accumulators in the epilogue.
 #include "common.h"
 #include "grouped.h"
 #include "kernels.h"
@@ -35,180 +35,19 @@
 namespace moe {
 namespace {
 
-constexpr int TBM = 128;  // activation rows per tile
-constexpr int TNB = 256;  // weight rows per tile
-constexpr int TBK = 64;   // k per LDS stage (8 chunks of 16 bytes per row)
-
-MOE_DEV int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
-
-// Stage loaders, written as macros so that the per-thread pointer and
-// register arrays are indexed only with unrolled constants (and stay in VGPRs).
-#define LOAD_GLOBAL(k0)                                                              \
-  do {                                                                               \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) ra[i] =                            \
-        *reinterpret_cast<const u32x4*>(aptr[i] + (k0));                             \
-    _Pragma("unroll") for (int i = 0; i < NBL; ++i) rb[i] =                          \
-        *reinterpret_cast<const u32x4*>(bptr[i] + (WT == WT_I8 ? (k0) : 2 * (k0)));  \
-  } while (0)
-
-#define STORE_LDS(buf)                                                               \
-  do {                                                                               \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                    \
-        sA[buf][swz((tid >> 3) + 32 * i, lc)] = ra[i];                               \
-    if (WT == WT_I8) {                                                               \
-      _Pragma("unroll") for (int i = 0; i < NBL; ++i) {                              \
-        const int r_ = (tid >> 2) + 64 * i, c16_ = tid & 3;                          \
-        const u32x4 lo_ = i8x8_to_bf16x8(rb[i].x, rb[i].y);                          \
-        const u32x4 hi_ = i8x8_to_bf16x8(rb[i].z, rb[i].w);                          \
-        sB[buf][swz(r_, 2 * c16_)] = lo_;                                            \
-        sB[buf][swz(r_, 2 * c16_ + 1)] = hi_;                                        \
-      }                                                                              \
-    } else {                                                                         \
-      _Pragma("unroll") for (int i = 0; i < NBL; ++i)                                \
-          sB[buf][swz((tid >> 3) + 32 * i, lc)] = rb[i];                             \
-    }                                                                                \
-  } while (0)
-
-template <bool GATEUP, int WT>
-__global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a, uint32_t n_ntiles) {
-  __shared__ u32x4 sA[2][TBM * 8];
-  __shared__ u32x4 sB[2][TNB * 8];
-
-  GroupedTile tile;
-  const uint32_t lin = xcd_swizzle(blockIdx.x, gridDim.x);
-  if (!grouped_tile(a.offsets, a.E, TBM, n_ntiles, lin, tile)) return;
-
-  const int N = GATEUP ? a.F : a.H;   // output columns
-  const int K = GATEUP ? a.H : a.F;
-  constexpr int BNO = GATEUP ? 128 : 256;
-  const int n0 = tile.nt * BNO;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int e = tile.e;
-
-  // ---- global -> register loaders -------------------------------------
-  const int lc = tid & 7;  // 16-byte chunk within a 64-wide k slice (bf16)
-  const uint16_t* aptr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min(tile.m0 + (tid >> 3) + 32 * i, tile.m_end - 1);
-    if (GATEUP) {
-      const int64_t t = a.perm[r] / a.k;
-      aptr[i] = static_cast<const uint16_t*>(a.x) + t * a.H + lc * 8;
-    } else {
-      aptr[i] = static_cast<const uint16_t*>(a.h) + (int64_t)r * a.F + lc * 8;
-    }
-  }
-  constexpr int NBL = WT == WT_I8 ? 4 : 8;  // B loads per thread per stage
-  const char* bptr[NBL];
-#pragma unroll
-  for (int i = 0; i < NBL; ++i) {
-    const int r = WT == WT_I8 ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;  // weight row in tile
-    const char* base;
-    int n;
-    if (GATEUP) {
-      n = n0 + (r & 127);
-      base = static_cast<const char*>(r < 128 ? a.wg : a.wu);
-    } else {
-      n = n0 + r;
-      base = static_cast<const char*>(a.wd);
-    }
-    n = min(n, N - 1);
-    const int64_t elem = ((int64_t)e * N + n) * K;
-    if (WT == WT_I8)
-      bptr[i] = base + elem + (tid & 3) * 16;
-    else
-      bptr[i] = base + (elem + lc * 8) * 2;
-  }
-
-  u32x4 ra[4], rb[NBL];
-  // ---- MFMA main loop -------------------------------------------------
-  const int wm = wave >> 1, wn = wave & 1;
-  int brow[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    brow[s] = GATEUP ? (s < 2 ? wn * 64 + s * 32 : 128 + wn * 64 + (s - 2) * 32)
-                     : wn * 128 + s * 32;
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
-
-  const int KT = K / TBK;
-  LOAD_GLOBAL(0);
-  STORE_LDS(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) LOAD_GLOBAL((kt + 1) * TBK);
-#pragma unroll
-    for (int ks = 0; ks < TBK / 16; ++ks) {
-      const int chunk = ks * 2 + (lane >> 5);
-      bf16x8 af[2], bfv[4];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = as_bf16x8(sA[buf][swz(wm * 64 + mi * 32 + (lane & 31), chunk)]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bfv[s] = as_bf16x8(sB[buf][swz(brow[s] + (lane & 31), chunk)]);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc[mi][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfv[s], acc[mi][s], 0, 0, 0);
-    }
-    if (kt + 1 < KT) STORE_LDS(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue ---------------------------------------------------------
-  // 32x32 accumulator layout: lane l holds column l%32; register v holds row
-  // 8*(v/4) + 4*(l/32) + v%4.
-  const int jcol = lane & 31;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = tile.m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= tile.m_end) continue;
-      if (GATEUP) {
-        uint16_t* hrow = static_cast<uint16_t*>(a.h) + (int64_t)r * a.F;
-#pragma unroll
-        for (int si = 0; si < 2; ++si) {
-          const int n = n0 + wn * 64 + si * 32 + jcol;
-          if (n >= N) continue;
-          float g = acc[mi][si][v], u = acc[mi][si + 2][v];
-          if (WT == WT_I8) {
-            g *= a.sg[(int64_t)e * a.F + n];
-            u *= a.su[(int64_t)e * a.F + n];
-          }
-          hrow[n] = f32_to_bf16_bits(swiglu(g, u));
-        }
-      } else {
-        uint16_t* yrow = static_cast<uint16_t*>(a.y) + (int64_t)r * a.H;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int n = n0 + wn * 128 + s * 32 + jcol;
-          if (n >= N) continue;
-          float y = acc[mi][s][v];
-          if (WT == WT_I8) y *= a.sd[(int64_t)e * a.H + n];
-          yrow[n] = f32_to_bf16_bits(y);
-        }
-      }
-    }
-  }
-}
-
-
 // ---------------------------------------------------------------------------
-// bf16 weights: direct-to-LDS pipelined kernel
+// direct-to-LDS pipelined grouped GEMM
 // ---------------------------------------------------------------------------
 constexpr int MBM = 256;   // activation rows per tile
 constexpr int MNB = 256;   // weight rows per tile
 constexpr int MBK = 64;    // k per LDS stage
-constexpr int MWM = 4, MWN = 2, MNW = MWM * MWN;   // wave grid
-constexpr int MLPW = MBM * 8 / 64 / MNW;           // LDS-DMA loads per wave per operand per stage
+constexpr int MNW = 8;                             // waves per work-group
+constexpr int MLPW = MBM * 8 / 64 / MNW;           // A LDS-DMA loads per wave per stage
+// wave grid (rows x weight rows): 4 x 2 for bf16 weights; 2 x 4 for int8, so
+// that each converted int8 operand is shared by fewer waves (the conversion
+// runs on the VALU once per wave that uses the operand)
+template <int WT> struct WaveGrid { static constexpr int M = 4, N = 2; };
+template <> struct WaveGrid<WT_I8> { static constexpr int M = 2, N = 4; };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -237,14 +76,18 @@ MOE_DEV void block_sync() {
   asm volatile("" ::: "memory");
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int WT>
 __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t n_ntiles) {
-  constexpr int CH = MBK / 8;                 // 16-byte chunks per LDS row
+  constexpr bool I8 = WT == WT_I8;
+  constexpr int CH = MBK / 8;                   // 16-byte chunks per A row (bf16)
+  constexpr int BCH = I8 ? MBK / 16 : MBK / 8;  // 16-byte chunks per B row (int8 or bf16)
+  constexpr int LPWB = MNB * BCH / 64 / MNW;    // B LDS-DMA loads per wave per stage
+  constexpr int MWM = WaveGrid<WT>::M, MWN = WaveGrid<WT>::N;
   constexpr int MW = MBM / MWM, NWR = MNB / MWN;
-  constexpr int MI = MW / 32, NI = NWR / 32;  // 2 x 4 accumulators
+  constexpr int MI = MW / 32, NI = NWR / 32;    // 8 accumulators: 2 x 4 (bf16) or 4 x 2 (int8)
   constexpr int NKS = MBK / 16;
   // one LDS variable per stage: the A tile then the B tile
-  __shared__ u32x4 sT0[(MBM + MNB) * CH], sT1[(MBM + MNB) * CH];
+  __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
   u32x4* const SA[2] = {sT0, sT1};
   u32x4* const SB[2] = {sT0 + MBM * CH, sT1 + MBM * CH};
 
@@ -257,10 +100,11 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   const int n0 = tile.nt * BNO;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, e = tile.e;
 
-  // LDS chunk q of a stage holds row q / CH, physical chunk q % CH, which is
-  // logical k-chunk (q % CH) ^ ((row >> 1) & 7)
+  // Swizzles. A (bf16, 8 chunks per row): chunk c of row r sits at physical
+  // chunk c ^ ((r >> 1) & 7). B int8 (4 chunks per row): c ^ ((r >> 2) & 3).
+  // Either way the 16 rows read by one 16-lane group hit 16 distinct banks.
   const uint16_t* asrc[MLPW];
-  const uint16_t* bsrc[MLPW];
+  const char* bsrc[LPWB];
 #pragma unroll
   for (int j = 0; j < MLPW; ++j) {
     const int q = (MLPW * wave + j) * 64 + lane;
@@ -270,17 +114,23 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
       asrc[j] = static_cast<const uint16_t*>(a.x) + (int64_t)(a.perm[row] / a.k) * a.H + c * 8;
     else
       asrc[j] = static_cast<const uint16_t*>(a.h) + (int64_t)row * a.F + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < LPWB; ++j) {
+    const int q = (LPWB * wave + j) * 64 + lane;
+    const int r = q / BCH;
+    const int c = I8 ? (q % BCH) ^ ((r >> 2) & 3) : (q % BCH) ^ ((r >> 1) & 7);
     int n;
-    const uint16_t* base;
+    const char* base;
     if (GATEUP) {
       n = n0 + (r & (MNB / 2 - 1));
-      base = static_cast<const uint16_t*>(r < MNB / 2 ? a.wg : a.wu);
+      base = static_cast<const char*>(r < MNB / 2 ? a.wg : a.wu);
     } else {
       n = n0 + r;
-      base = static_cast<const uint16_t*>(a.wd);
+      base = static_cast<const char*>(a.wd);
     }
     n = min(n, N - 1);
-    bsrc[j] = base + ((int64_t)e * N + n) * K + c * 8;
+    bsrc[j] = base + (((int64_t)e * N + n) * K) * (I8 ? 1 : 2) + c * 16;
   }
 
   const int wm = wave / MWN, wn = wave % MWN;
@@ -301,26 +151,34 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
       for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
   bf16x8 fa[2][MI], fb[2][NI];
 
-#define MOE_ISSUE(ST, K0)                                              \
-  do {                                                                 \
-    _Pragma("unroll") for (int j = 0; j < MLPW; ++j) {                 \
-      lds_dma16(asrc[j] + (K0), SA[ST] + (MLPW * wave + j) * 64);      \
-      lds_dma16(bsrc[j] + (K0), SB[ST] + (MLPW * wave + j) * 64);      \
-    }                                                                  \
+#define MOE_ISSUE(ST, K0)                                                    \
+  do {                                                                       \
+    _Pragma("unroll") for (int j = 0; j < MLPW; ++j)                         \
+      lds_dma16(asrc[j] + (K0), SA[ST] + (MLPW * wave + j) * 64);            \
+    _Pragma("unroll") for (int j = 0; j < LPWB; ++j)                         \
+      lds_dma16(bsrc[j] + (K0) * (I8 ? 1 : 2), SB[ST] + (LPWB * wave + j) * 64); \
   } while (0)
 #define MOE_LOADF(SLOT, ST, KS)                                                        \
   do {                                                                                 \
     const int chunk_ = (KS) * 2 + (lane >> 5);                                         \
     _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) fa[SLOT][mi] = as_bf16x8(        \
         SA[ST][arow[mi] * CH + (chunk_ ^ ((arow[mi] >> 1) & 7))]);                     \
-    _Pragma("unroll") for (int s = 0; s < NI; ++s) fb[SLOT][s] = as_bf16x8(            \
-        SB[ST][brow[s] * CH + (chunk_ ^ ((brow[s] >> 1) & 7))]);                       \
+    if (I8) {                                                                          \
+      _Pragma("unroll") for (int s = 0; s < NI; ++s) {                                 \
+        const uint2 q_ = reinterpret_cast<const uint2*>(                               \
+            SB[ST] + brow[s] * BCH + ((KS) ^ ((brow[s] >> 2) & 3)))[lane >> 5];        \
+        fb[SLOT][s] = as_bf16x8(i8x8_to_bf16x8(q_.x, q_.y));                           \
+      }                                                                                \
+    } else {                                                                           \
+      _Pragma("unroll") for (int s = 0; s < NI; ++s) fb[SLOT][s] = as_bf16x8(          \
+          SB[ST][brow[s] * BCH + (chunk_ ^ ((brow[s] >> 1) & 7))]);                    \
+    }                                                                                  \
   } while (0)
 
   const int KT = K / MBK;
   MOE_ISSUE(0, 0);
   if (KT > 1) MOE_ISSUE(1, MBK);
-  if (KT > 1) wait_vmcnt<2 * MLPW>(); else wait_vmcnt<0>();
+  if (KT > 1) wait_vmcnt<MLPW + LPWB>(); else wait_vmcnt<0>();
   block_sync();
   MOE_LOADF(0, 0, 0);
   for (int kt0 = 0; kt0 < KT; kt0 += 2) {
@@ -375,36 +233,38 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
 #pragma unroll
         for (int si = 0; si < NI / 2; ++si) {
           const int n = n0 + wn * (NWR / 2) + si * 32 + jcol;
-          if (n < N) hrow[n] = f32_to_bf16_bits(swiglu(acc[mi][si][v], acc[mi][si + NI / 2][v]));
+          if (n < N) {
+            float g = acc[mi][si][v], u = acc[mi][si + NI / 2][v];
+            if (I8) {
+              g *= a.sg[(int64_t)e * a.F + n];
+              u *= a.su[(int64_t)e * a.F + n];
+            }
+            hrow[n] = f32_to_bf16_bits(swiglu(g, u));
+          }
         }
       } else {
         uint16_t* yrow = static_cast<uint16_t*>(a.y) + (int64_t)r * a.H;
 #pragma unroll
         for (int s = 0; s < NI; ++s) {
           const int n = n0 + wn * NWR + s * 32 + jcol;
-          if (n < N) yrow[n] = f32_to_bf16_bits(acc[mi][s][v]);
+          if (n < N)
+            yrow[n] = f32_to_bf16_bits(I8 ? acc[mi][s][v] * a.sd[(int64_t)e * a.H + n]
+                                          : acc[mi][s][v]);
         }
       }
     }
   }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int WT>
 hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
   const uint32_t nt = GATEUP ? (uint32_t)((a.F + MNB / 2 - 1) / (MNB / 2))
                              : (uint32_t)((a.H + MNB - 1) / MNB);
-  hipLaunchKernelGGL((ffn_mfma_kernel<GATEUP>), dim3(grouped_grid(a.T * a.k, a.E, MBM, nt)),
+  hipLaunchKernelGGL((ffn_mfma_kernel<GATEUP, WT>), dim3(grouped_grid(a.T * a.k, a.E, MBM, nt)),
                      dim3(MNW * 64), 0, s, a, nt);
   return hipGetLastError();
 }
 
-template <bool GATEUP, int WT>
-hipError_t launch_one(const FfnArgs& a, hipStream_t s) {
-  const uint32_t nt = GATEUP ? (uint32_t)((a.F + 127) / 128) : (uint32_t)((a.H + 255) / 256);
-  hipLaunchKernelGGL((ffn_tiled_kernel<GATEUP, WT>), dim3(grouped_grid(a.T * a.k, a.E, TBM, nt)),
-                     dim3(256), 0, s, a, nt);
-  return hipGetLastError();
-}
 
 }  // namespace
 
@@ -415,11 +275,11 @@ size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt) {
 }
 
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
-  return wt == WT_I8 ? launch_one<true, WT_I8>(a, s) : launch_mfma<true>(a, s);
+  return wt == WT_I8 ? launch_mfma<true, WT_I8>(a, s) : launch_mfma<true, WT_BF16>(a, s);
 }
 
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
-  return wt == WT_I8 ? launch_one<false, WT_I8>(a, s) : launch_mfma<false>(a, s);
+  return wt == WT_I8 ? launch_mfma<false, WT_I8>(a, s) : launch_mfma<false, WT_BF16>(a, s);
 }
 
 }  // namespace moe
