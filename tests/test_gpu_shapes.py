@@ -1,0 +1,124 @@
+"""GPU parity for shapes beyond the Grok-1 defaults and for the ABI's stage
+entry points: other expert counts and k, the decode/tiled kernel boundary
+(T = 16 / 17), empty experts, and moe_expert_gate_up / moe_expert_down
+called on their own."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (check_close, check_dispatch_equal, check_routing, dev_tensor,
+                         host_array, log, out_as_f64, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import sparse_moe_transformer_top_amd as m
+    m.load_library()
+    return m
+
+
+def run_layer(moe, cfg, inp, d):
+    out, ax = moe.moe_layer_forward(d["x"], d["wr"], d["wg"], d["wu"], d["wd"], k=cfg.k,
+                                    capacity_factor=cfg.capacity_factor, s_gate=d["sg"],
+                                    s_up=d["su"], s_down=d["sd"], aux=True)
+    torch.cuda.synchronize()
+    res = oracle.layer_forward(inp.x, cfg.act, inp.wr, inp.wg, inp.wu, inp.wd, cfg.wdt, k=cfg.k,
+                               capacity_factor=cfg.capacity_factor, sg=inp.sg, su=inp.su,
+                               sd=inp.sd)
+    return out, ax, res
+
+
+SHAPES = [
+    # name, T, H, F, E, k, act, wdt, cf
+    ("e16_k4", 200, 256, 384, 16, 4, "bf16", "bf16", None),
+    ("e16_k4_dec", 12, 256, 384, 16, 4, "bf16", "bf16", None),
+    ("e4_k1", 150, 192, 320, 4, 1, "bf16", "bf16", None),
+    ("e4_k1_cap", 150, 192, 320, 4, 1, "bf16", "i8", 1.1),
+    ("e12_k3_f32", 70, 128, 256, 12, 3, "f32", "f32", 2.0),
+    ("t16_dec", 16, 512, 640, 8, 2, "bf16", "bf16", None),
+    ("t17_tiled", 17, 512, 640, 8, 2, "bf16", "bf16", None),
+    ("t16_dec_i8", 16, 512, 640, 8, 2, "bf16", "i8", None),
+    ("e2_k2", 90, 256, 256, 2, 2, "bf16", "bf16", 0.75),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_layer_shapes(moe, shape):
+    name, T, H, F, E, k, act, wdt, cf = shape
+    cfg = synth.LayerConfig(name, T=T, H=H, F=F, E=E, k=k, act=act, wdt=wdt,
+                            capacity_factor=cf, seed=len(name))
+    log(f"shape {name}")
+    inp = synth.generate_host(cfg)
+    out, ax, res = run_layer(moe, cfg, inp, to_device(inp))
+    diff = check_routing(host_array(ax["topk_idx"]), host_array(ax["topk_w"]), res.routing)
+    assert not diff.any()
+    assert np.array_equal(host_array(ax["counts"]), res.disp.counts)
+    assert np.array_equal(host_array(ax["offsets"]), res.disp.offsets)
+    assert np.array_equal(host_array(ax["dropped"]), res.disp.dropped)
+    check_close(out_as_f64(out), res.out, act, name)
+
+
+def test_dispatch_on_oracle_indices_general_k(moe):
+    rng = np.random.default_rng(3)
+    for T, E, k, cf in ((3000, 16, 4, 1.0), (2500, 4, 1, 1.5), (777, 12, 3, None)):
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        got = moe.moe_dispatch(dev_tensor(idx, "i32"), E, cf)
+        torch.cuda.synchronize()
+        check_dispatch_equal({n: host_array(v) for n, v in got.items()}, oracle.dispatch(idx, E, cf))
+
+
+@pytest.mark.parametrize("name", ["p_bf16", "p_i8", "p_bf16_dec", "p_i8_dec"])
+def test_stage_entry_points(moe, name):
+    # moe_expert_gate_up then moe_expert_down, each against the oracle
+    cfg = synth.get_config(name)
+    inp = synth.generate_host(cfg)
+    d = to_device(inp)
+    res = oracle.layer_forward(inp.x, cfg.act, inp.wr, inp.wg, inp.wu, inp.wd, cfg.wdt, k=cfg.k,
+                               sg=inp.sg, su=inp.su, sd=inp.sd)
+    perm = dev_tensor(res.disp.perm, "i32")
+    off = dev_tensor(res.disp.offsets, "i32")
+    h = moe.moe_expert_gate_up(d["x"], perm, off, cfg.k, d["wg"], d["wu"], d["sg"], d["su"])
+    y = moe.moe_expert_down(h, off, cfg.T, cfg.k, d["wd"], d["sd"])
+    torch.cuda.synchronize()
+    n = int(res.disp.offsets[-1])
+    x64 = oracle.widen(inp.x, cfg.act)
+    hg, yg = out_as_f64(h)[:n], out_as_f64(y)[:n]
+    h_ref = np.zeros_like(hg)
+    y_ref = np.zeros_like(yg)
+    for e in range(cfg.E):
+        r0, r1 = res.disp.offsets[e], res.disp.offsets[e + 1]
+        if r1 == r0:
+            continue
+        sc = (lambda a: None if a is None else a[e])
+        tok = res.disp.perm[r0:r1] // cfg.k
+        h_ref[r0:r1] = oracle.expert_hidden(x64[tok], oracle.widen(inp.wg[e], cfg.wdt, sc(inp.sg)),
+                                            oracle.widen(inp.wu[e], cfg.wdt, sc(inp.su)))
+        y_ref[r0:r1] = hg[r0:r1] @ oracle.widen(inp.wd[e], cfg.wdt, sc(inp.sd)).T
+    check_close(hg, h_ref, cfg.act, "gate_up")
+    check_close(yg, y_ref, cfg.act, "down")
+
+
+@pytest.mark.parametrize("name", ["p_bf16", "p_bf16_dec", "p_i8"])
+def test_determinism_each_path(moe, name):
+    cfg = synth.get_config(name)
+    d = to_device(synth.generate_host(cfg))
+    outs = [moe.moe_layer_forward(d["x"], d["wr"], d["wg"], d["wu"], d["wd"], k=cfg.k,
+                                  s_gate=d["sg"], s_up=d["su"], s_down=d["sd"]) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_router_logits_output(moe):
+    cfg = synth.get_config("p_skew")
+    inp = synth.generate_host(cfg)
+    d = to_device(inp)
+    idx, w, logits = moe.moe_router_topk(d["x"], d["wr"], 2, return_logits=True)
+    torch.cuda.synchronize()
+    l32, l64 = oracle.router_logits(oracle.widen(inp.x, cfg.act), inp.wr)
+    lg = host_array(logits).astype(np.float64)
+    assert np.max(np.abs(lg - l64) / np.maximum(1.0, np.abs(l64).max(axis=1, keepdims=True))) < 2e-5
