@@ -15,7 +15,8 @@
 //
 // Two kernels, 1024 tokens per work-group: (1) per-block expert histogram;
 // (2) every block derives its starting rank per expert from the histograms of
-// the blocks before it, ranks its tokens and scatters.
+// the blocks before it, ranks its tokens and scatters. Up to 1024 tokens the
+// first kernel is skipped.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,42 +43,20 @@ __global__ __launch_bounds__(kBlockTokens) void dispatch_hist_kernel(
   if (threadIdx.x < E) hist[(int64_t)blockIdx.x * E + threadIdx.x] = s_hist[threadIdx.x];
 }
 
+// With nblk == 1 (all tokens in this block) the histogram pass is skipped and
+// the block's own ballot counts are the totals.
 __global__ __launch_bounds__(kBlockTokens) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int E, int k, int64_t cap, int nblk,
     const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ slot_row, uint8_t* __restrict__ dropped) {
   __shared__ int32_t s_base[kMaxE];                 // rank of this block's first token per expert
+  __shared__ int32_t s_total[kMaxE];                // assignments per expert over all blocks
   __shared__ int32_t s_off[kMaxE + 1];              // row offsets per expert
   __shared__ int32_t s_wcnt[kMaxE][kWavesPerBlock];  // per-wave counts -> exclusive wave bases
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int blk = blockIdx.x;
-
-  if (tid < E) {
-    int32_t base = 0, total = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t c = hist[(int64_t)b * E + tid];
-      if (b < blk) base += c;
-      total += c;
-    }
-    s_base[tid] = base;
-    s_wcnt[tid][0] = total;   // borrowed until the scan below; rewritten later
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int32_t total = s_wcnt[e][0];
-      const int32_t kept = (cap >= 0 && total > cap) ? (int32_t)cap : total;
-      s_off[e] = run;
-      if (blk == 0) { counts[e] = total; offsets[e] = run; }
-      run += kept;
-    }
-    s_off[E] = run;
-    if (blk == 0) offsets[E] = run;
-  }
-  __syncthreads();
 
   const int64_t t = (int64_t)blk * kBlockTokens + tid;
   const bool valid = t < T;
@@ -90,6 +69,7 @@ __global__ __launch_bounds__(kBlockTokens) void dispatch_scatter_kernel(
     }
   }
 
+  // in-block stable ranks: ballot per expert, popcount of the lower lanes
   const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
   int lrank[4] = {0, 0, 0, 0};
   for (int e = 0; e < E; ++e) {
@@ -111,6 +91,30 @@ __global__ __launch_bounds__(kBlockTokens) void dispatch_scatter_kernel(
       s_wcnt[tid][w] = run;
       run += c;
     }
+    int32_t base = 0, total = run;
+    if (nblk > 1) {
+      total = 0;
+      for (int b = 0; b < nblk; ++b) {
+        const int32_t c = hist[(int64_t)b * E + tid];
+        if (b < blk) base += c;
+        total += c;
+      }
+    }
+    s_base[tid] = base;
+    s_total[tid] = total;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int e = 0; e < E; ++e) {
+      const int32_t total = s_total[e];
+      const int32_t kept = (cap >= 0 && total > cap) ? (int32_t)cap : total;
+      s_off[e] = run;
+      if (blk == 0) { counts[e] = total; offsets[e] = run; }
+      run += kept;
+    }
+    s_off[E] = run;
+    if (blk == 0) offsets[E] = run;
   }
   __syncthreads();
 
@@ -163,10 +167,12 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int E, int k, int64_t 
                            uint8_t* dropped, void* ws, hipStream_t s) {
   const int nblk = (int)((T + kBlockTokens - 1) / kBlockTokens);
   int32_t* hist = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nblk), dim3(kBlockTokens), 0, s, idx, T, E, k,
-                     hist);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (nblk > 1) {
+    hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nblk), dim3(kBlockTokens), 0, s, idx, T, E, k,
+                       hist);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(kBlockTokens), 0, s, idx, T, E, k,
                      cap, nblk, hist, counts, offsets, perm, slot_row, dropped);
   return hipGetLastError();

@@ -6,19 +6,22 @@
 // (section "Routing: top-2 without auxiliary loss", grok_router_forward;
 // section "The high-level architecture", GrokMoELayer.forward).
 //
-// Mapping: a work-group has 4 waves, a wave owns kTokPerWave tokens. Lanes
-// split the hidden dimension into 8-element chunks (16-byte loads of bf16 x,
-// 32 bytes of the float32 router row per expert); each router chunk is loaded
-// once per wave and reused for all the wave's tokens. Partial dot products are
-// reduced across the 64 lanes with an xor butterfly (fixed order, identical
-// result on every lane), so logits are deterministic.
+// Mapping: a work-group owns kTokPerBlock tokens and its 4 waves split the
+// hidden dimension into 4 contiguous quarters, so that a decode batch of a few
+// tokens still runs 4 short dependency chains per token group instead of one
+// long one. Lanes split a wave's quarter into 8-element chunks (16-byte loads
+// of bf16 x, 32 bytes of the float32 router row per expert); each router
+// chunk is loaded once and reused for all the block's tokens. Partial dot
+// products are reduced across the 64 lanes with an xor butterfly (fixed
+// order, identical on every lane) and then across the 4 waves through LDS in
+// wave order, so logits are deterministic.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTokPerWave = 4;
+constexpr int kTokPerBlock = 4;
 constexpr int kWaves = 4;
 
 template <int ACT>
@@ -83,18 +86,23 @@ template <int EC, int ACT>
 __global__ __launch_bounds__(kWaves * 64) void router_topk_kernel(
     const void* __restrict__ x, const float* __restrict__ wr, int64_t T, int H, int E, int k,
     int32_t* __restrict__ idx, float* __restrict__ w, float* __restrict__ logits) {
+  __shared__ float part[kWaves][kTokPerBlock][EC];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t t0 = ((int64_t)blockIdx.x * kWaves + wave) * kTokPerWave;
-  if (t0 >= T) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kTokPerBlock;
 
-  float acc[kTokPerWave][EC];
+  float acc[kTokPerBlock][EC];
 #pragma unroll
-  for (int i = 0; i < kTokPerWave; ++i)
+  for (int i = 0; i < kTokPerBlock; ++i)
 #pragma unroll
     for (int e = 0; e < EC; ++e) acc[i][e] = 0.f;
 
-  for (int h0 = lane * 8; h0 < H; h0 += 64 * 8) {
+  // this wave's quarter of the hidden dimension, in 8-element chunks
+  const int chunks = H / 8;
+  const int c_begin = (chunks * wave) / kWaves, c_end = (chunks * (wave + 1)) / kWaves;
+#pragma unroll 2
+  for (int c = c_begin + lane; c < c_end; c += 64) {
+    const int h0 = c * 8;
     float wv[EC][8];
 #pragma unroll
     for (int e = 0; e < EC; ++e) {
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(kWaves * 64) void router_topk_kernel(
       }
     }
 #pragma unroll
-    for (int tt = 0; tt < kTokPerWave; ++tt) {
+    for (int tt = 0; tt < kTokPerBlock; ++tt) {
       const int64_t t = t0 + tt;
       if (t < T) {
         float xv[8];
@@ -123,21 +131,37 @@ __global__ __launch_bounds__(kWaves * 64) void router_topk_kernel(
   }
 
 #pragma unroll
-  for (int tt = 0; tt < kTokPerWave; ++tt)
+  for (int tt = 0; tt < kTokPerBlock; ++tt)
 #pragma unroll
     for (int e = 0; e < EC; ++e) acc[tt][e] = wave_sum_xor(acc[tt][e]);
-
+  if (lane == 0) {
 #pragma unroll
-  for (int tt = 0; tt < kTokPerWave; ++tt) {
-    if (lane == tt && t0 + tt < T) select_topk<EC>(acc[tt], E, k, t0 + tt, idx, w, logits);
+    for (int tt = 0; tt < kTokPerBlock; ++tt)
+#pragma unroll
+      for (int e = 0; e < EC; ++e) part[wave][tt][e] = acc[tt][e];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int tt = 0; tt < kTokPerBlock; ++tt) {
+    if (lane == tt && t0 + tt < T) {
+      float l[EC];
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        float v = part[0][tt][e];
+#pragma unroll
+        for (int wv = 1; wv < kWaves; ++wv) v += part[wv][tt][e];
+        l[e] = v;
+      }
+      select_topk<EC>(l, E, k, t0 + tt, idx, w, logits);
+    }
   }
 }
 
 template <int EC>
 hipError_t launch_ec(const void* x, Act act, const float* wr, int64_t T, int H, int E, int k,
                      int32_t* idx, float* w, float* logits, hipStream_t s) {
-  const int64_t per_block = (int64_t)kWaves * kTokPerWave;
-  const dim3 grid((unsigned)((T + per_block - 1) / per_block));
+  const dim3 grid((unsigned)((T + kTokPerBlock - 1) / kTokPerBlock));
   if (act == ACT_BF16)
     hipLaunchKernelGGL((router_topk_kernel<EC, ACT_BF16>), grid, dim3(kWaves * 64), 0, s, x, wr,
                        T, H, E, k, idx, w, logits);

@@ -64,7 +64,9 @@ def test_layer_shapes(moe, shape):
 
 def test_dispatch_on_oracle_indices_general_k(moe):
     rng = np.random.default_rng(3)
-    for T, E, k, cf in ((3000, 16, 4, 1.0), (2500, 4, 1, 1.5), (777, 12, 3, None)):
+    # 1024 tokens fill exactly one dispatch block (single-kernel path); 1025 need two
+    for T, E, k, cf in ((3000, 16, 4, 1.0), (2500, 4, 1, 1.5), (777, 12, 3, None),
+                        (1024, 8, 2, 1.25), (1025, 8, 2, 1.25), (1, 8, 2, 1.25)):
         idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
         got = moe.moe_dispatch(dev_tensor(idx, "i32"), E, cf)
         torch.cuda.synchronize()
