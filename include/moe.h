@@ -31,7 +31,7 @@
  *     and no call copies data between host and device.
  *   - Shapes: T tokens (flattened batch*seq), H hidden, F expert dim, E
  *     experts, k experts per token. Supported: T >= 0, T*k < 2^31,
- *     1 <= E <= 16, 1 <= k <= min(E, 4), H >= 64 and F >= 64 with
+ *     1 <= E <= 16, 1 <= k <= min(E, 4), 64 <= H, F <= 2^20 with
  *     H % 64 == 0 and F % 64 == 0.
  *   - dtypes: activations (x, h, y_perm, out) are MOE_F32 or MOE_BF16; expert
  *     weights are MOE_F32 (with f32 activations), MOE_BF16 or MOE_I8 (with

@@ -62,6 +62,7 @@ moe_status check_shape(int64_t T, int32_t E, int32_t k) {
 moe_status check_dim(const char* name, int32_t v) {
   REQUIRE(v >= 1, MOE_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %d)", name, v);
   REQUIRE(v % 64 == 0, MOE_ERR_UNSUPPORTED, "%s=%d must be a multiple of 64", name, v);
+  REQUIRE(v <= (1 << 20), MOE_ERR_UNSUPPORTED, "%s=%d is above the supported 1048576", name, v);
   return ok();
 }
 

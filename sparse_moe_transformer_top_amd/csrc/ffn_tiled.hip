@@ -51,16 +51,35 @@ template <> struct WaveGrid<WT_I8> { static constexpr int M = 2, N = 4; };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// 64 lanes x 16 bytes from per-lane global addresses into LDS at l + 16*lane
-// (l wave-uniform). Written as asm because the compiler's wait-count pass,
-// unable to tell the two LDS stages apart, otherwise drains every outstanding
-// load before each LDS read; this kernel places its own vmcnt waits. The load
-// writes no VGPR.
-MOE_DEV void lds_dma16(const void* g, void* l) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t*)l;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+MOE_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void_t*)p; }
+
+// A wave-uniform pointer, held in scalar registers.
+MOE_DEV const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
+
+// 64 lanes x 16 bytes from global memory into LDS at byte address lds +
+// 16*lane (lds wave-uniform), written as asm because the compiler's
+// wait-count pass, unable to tell the two LDS stages apart, otherwise drains
+// every outstanding load before each LDS read; this kernel places its own
+// vmcnt waits. The load writes no VGPR. Two address forms: a scalar base plus
+// a per-lane 32-bit byte offset (below 2^31), or a per-lane 64-bit address.
+// m0 is named as clobbered on purpose: the asm sets it, and the compiler
+// keeps nothing in m0 in these kernels (checked in the generated code).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+MOE_DEV void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+MOE_DEV void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N) leaving the other counters untouched
 template <int N>
@@ -76,11 +95,14 @@ MOE_DEV void block_sync() {
   asm volatile("" ::: "memory");
 }
 
-template <bool GATEUP, int WT>
+// WIDE: the gathered activation rows are addressed with 64-bit per-lane
+// pointers (x larger than 2 GiB); otherwise with 32-bit offsets from x.
+template <bool GATEUP, int WT, bool WIDE>
 __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t n_ntiles) {
   constexpr bool I8 = WT == WT_I8;
+  constexpr int ESZ = I8 ? 1 : 2;               // weight element bytes
   constexpr int CH = MBK / 8;                   // 16-byte chunks per A row (bf16)
-  constexpr int BCH = I8 ? MBK / 16 : MBK / 8;  // 16-byte chunks per B row (int8 or bf16)
+  constexpr int BCH = MBK * ESZ / 16;           // 16-byte chunks per B row (int8 or bf16)
   constexpr int LPWB = MNB * BCH / 64 / MNW;    // B LDS-DMA loads per wave per stage
   constexpr int MWM = WaveGrid<WT>::M, MWN = WaveGrid<WT>::N;
   constexpr int MW = MBM / MWM, NWR = MNB / MWN;
@@ -90,47 +112,61 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
   u32x4* const SA[2] = {sT0, sT1};
   u32x4* const SB[2] = {sT0 + MBM * CH, sT1 + MBM * CH};
+  const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
 
+  uint32_t lin;
   GroupedTile tile;
-  const uint32_t lin = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (!xcd_tile_index(a.offsets, a.E, MBM, n_ntiles, lin)) return;
   if (!grouped_tile(a.offsets, a.E, MBM, n_ntiles, lin, tile)) return;
   const int N = GATEUP ? a.F : a.H;
   const int K = GATEUP ? a.H : a.F;
   constexpr int BNO = GATEUP ? MNB / 2 : MNB;  // output columns per tile
-  const int n0 = tile.nt * BNO;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, e = tile.e;
+  const int e = __builtin_amdgcn_readfirstlane(tile.e);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile.m0);
+  const int m_end = __builtin_amdgcn_readfirstlane(tile.m_end);
+  const int n0 = __builtin_amdgcn_readfirstlane(tile.nt * BNO);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Swizzles. A (bf16, 8 chunks per row): chunk c of row r sits at physical
   // chunk c ^ ((r >> 1) & 7). B int8 (4 chunks per row): c ^ ((r >> 2) & 3).
   // Either way the 16 rows read by one 16-lane group hit 16 distinct banks.
-  const uint16_t* asrc[MLPW];
-  const char* bsrc[LPWB];
+  //
+  // A: gathered x rows (gate/up) or this tile's h rows (down). The k offset
+  // goes into the scalar base.
+  const char* const abase = GATEUP ? uniform_ptr(a.x)
+                                   : uniform_ptr(static_cast<const char*>(a.h) +
+                                                 (int64_t)m0 * a.F * 2);
+  uint32_t aoff[MLPW];
+  const char* aptr[WIDE ? MLPW : 1];
 #pragma unroll
   for (int j = 0; j < MLPW; ++j) {
     const int q = (MLPW * wave + j) * 64 + lane;
     const int r = q / CH, c = (q % CH) ^ ((r >> 1) & 7);
-    const int row = min(tile.m0 + r, tile.m_end - 1);
-    if (GATEUP)
-      asrc[j] = static_cast<const uint16_t*>(a.x) + (int64_t)(a.perm[row] / a.k) * a.H + c * 8;
-    else
-      asrc[j] = static_cast<const uint16_t*>(a.h) + (int64_t)row * a.F + c * 8;
+    const int row = min(m0 + r, m_end - 1);
+    if (GATEUP) {
+      const int64_t tok = a.perm[row] / a.k;
+      if (WIDE) aptr[WIDE ? j : 0] = static_cast<const char*>(a.x) + tok * a.H * 2 + c * 16;
+      else aoff[j] = (uint32_t)tok * (uint32_t)(a.H * 2) + c * 16;
+    } else {
+      aoff[j] = (uint32_t)(row - m0) * (uint32_t)(a.F * 2) + c * 16;
+    }
   }
+  // B: one weight matrix per wave. Each wave loads 32 consecutive B-tile
+  // rows; with GATEUP, waves [0, MNW/2) load the gate rows (tile rows
+  // [0, MNB/2)) and the others the up rows of the same output columns.
+  const void* const wmat = GATEUP ? (wave < MNW / 2 ? a.wg : a.wu) : a.wd;
+  const char* const bbase =
+      uniform_ptr(static_cast<const char*>(wmat) + ((int64_t)e * N + n0) * K * ESZ);
+  uint32_t boff[LPWB];
 #pragma unroll
   for (int j = 0; j < LPWB; ++j) {
     const int q = (LPWB * wave + j) * 64 + lane;
     const int r = q / BCH;
     const int c = I8 ? (q % BCH) ^ ((r >> 2) & 3) : (q % BCH) ^ ((r >> 1) & 7);
-    int n;
-    const char* base;
-    if (GATEUP) {
-      n = n0 + (r & (MNB / 2 - 1));
-      base = static_cast<const char*>(r < MNB / 2 ? a.wg : a.wu);
-    } else {
-      n = n0 + r;
-      base = static_cast<const char*>(a.wd);
-    }
-    n = min(n, N - 1);
-    bsrc[j] = base + (((int64_t)e * N + n) * K) * (I8 ? 1 : 2) + c * 16;
+    const int rr = GATEUP ? (r & (MNB / 2 - 1)) : r;
+    const int n = min(n0 + rr, N - 1) - n0;
+    boff[j] = (uint32_t)n * (uint32_t)(K * ESZ) + c * 16;
   }
 
   const int wm = wave / MWN, wn = wave % MWN;
@@ -151,12 +187,16 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
       for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
   bf16x8 fa[2][MI], fb[2][NI];
 
-#define MOE_ISSUE(ST, K0)                                                    \
-  do {                                                                       \
-    _Pragma("unroll") for (int j = 0; j < MLPW; ++j)                         \
-      lds_dma16(asrc[j] + (K0), SA[ST] + (MLPW * wave + j) * 64);            \
-    _Pragma("unroll") for (int j = 0; j < LPWB; ++j)                         \
-      lds_dma16(bsrc[j] + (K0) * (I8 ? 1 : 2), SB[ST] + (LPWB * wave + j) * 64); \
+#define MOE_ISSUE(ST, K0)                                                               \
+  do {                                                                                  \
+    const uint32_t la_ = ((ST) ? L1 : L0) + (uint32_t)(MLPW * wave) * 1024u;            \
+    const uint32_t lb_ = ((ST) ? L1 : L0) + MBM * CH * 16 + (uint32_t)(LPWB * wave) * 1024u; \
+    _Pragma("unroll") for (int j = 0; j < MLPW; ++j) {                                  \
+      if (WIDE) lds_dma16(aptr[WIDE ? j : 0] + (K0) * 2, la_ + j * 1024);               \
+      else lds_dma16(abase + (K0) * 2, aoff[j], la_ + j * 1024);                        \
+    }                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < LPWB; ++j)                                    \
+      lds_dma16(bbase + (K0) * ESZ, boff[j], lb_ + j * 1024);                           \
   } while (0)
 #define MOE_LOADF(SLOT, ST, KS)                                                        \
   do {                                                                                 \
@@ -175,13 +215,16 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
     }                                                                                  \
   } while (0)
 
+  // K >= 64, so there is at least one stage; a do-while keeps the compiler
+  // from carrying a zero-trip copy of the accumulators across the loop
   const int KT = K / MBK;
   MOE_ISSUE(0, 0);
   if (KT > 1) MOE_ISSUE(1, MBK);
   if (KT > 1) wait_vmcnt<MLPW + LPWB>(); else wait_vmcnt<0>();
   block_sync();
   MOE_LOADF(0, 0, 0);
-  for (int kt0 = 0; kt0 < KT; kt0 += 2) {
+  int kt0 = 0;
+  do {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kt = kt0 + u;
@@ -215,7 +258,8 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
         }
       }
     }
-  }
+    kt0 += 2;
+  } while (kt0 < KT);
 #undef MOE_ISSUE
 #undef MOE_LOADF
 
@@ -226,8 +270,8 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int r = tile.m0 + wm * MW + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= tile.m_end) continue;
+      const int r = m0 + wm * MW + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (r >= m_end) continue;
       if (GATEUP) {
         uint16_t* hrow = static_cast<uint16_t*>(a.h) + (int64_t)r * a.F;
 #pragma unroll
@@ -256,15 +300,17 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   }
 }
 
-template <bool GATEUP, int WT>
+template <bool GATEUP, int WT, bool WIDE>
 hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
   const uint32_t nt = GATEUP ? (uint32_t)((a.F + MNB / 2 - 1) / (MNB / 2))
                              : (uint32_t)((a.H + MNB - 1) / MNB);
-  hipLaunchKernelGGL((ffn_mfma_kernel<GATEUP, WT>), dim3(grouped_grid(a.T * a.k, a.E, MBM, nt)),
-                     dim3(MNW * 64), 0, s, a, nt);
+  hipLaunchKernelGGL((ffn_mfma_kernel<GATEUP, WT, WIDE>),
+                     dim3(grouped_grid(a.T * a.k, a.E, MBM, nt)), dim3(MNW * 64), 0, s, a, nt);
   return hipGetLastError();
 }
 
+// 32-bit offsets from x reach the gathered rows while x is below 2 GiB
+bool x_needs_wide(const FfnArgs& a) { return (uint64_t)a.T * (uint64_t)a.H * 2 > (1ull << 31); }
 
 }  // namespace
 
@@ -275,11 +321,16 @@ size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt) {
 }
 
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
-  return wt == WT_I8 ? launch_mfma<true, WT_I8>(a, s) : launch_mfma<true, WT_BF16>(a, s);
+  if (x_needs_wide(a))
+    return wt == WT_I8 ? launch_mfma<true, WT_I8, true>(a, s)
+                       : launch_mfma<true, WT_BF16, true>(a, s);
+  return wt == WT_I8 ? launch_mfma<true, WT_I8, false>(a, s)
+                     : launch_mfma<true, WT_BF16, false>(a, s);
 }
 
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
-  return wt == WT_I8 ? launch_mfma<false, WT_I8>(a, s) : launch_mfma<false, WT_BF16>(a, s);
+  return wt == WT_I8 ? launch_mfma<false, WT_I8, false>(a, s)
+                     : launch_mfma<false, WT_BF16, false>(a, s);
 }
 
 }  // namespace moe

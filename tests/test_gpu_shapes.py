@@ -124,3 +124,29 @@ def test_router_logits_output(moe):
     l32, l64 = oracle.router_logits(oracle.widen(inp.x, cfg.act), inp.wr)
     lg = host_array(logits).astype(np.float64)
     assert np.max(np.abs(lg - l64) / np.maximum(1.0, np.abs(l64).max(axis=1, keepdims=True))) < 2e-5
+
+
+def test_gather_over_2gib_of_x(moe):
+    # x above 2 GiB: the gate/up kernel addresses the gathered rows with
+    # 64-bit pointers instead of 32-bit offsets from x
+    from synth.device import generate_device
+    cfg = synth.LayerConfig("x_2gib", T=180_000, H=6144, F=128, E=8, k=2, seed=11)
+    assert cfg.T * cfg.H * 2 > 2 ** 31
+    log(f"x over 2 GiB: T={cfg.T} H={cfg.H} F={cfg.F}")
+    d = generate_device(cfg, "cuda")
+    out, ax = moe.moe_layer_forward(d.x, d.wr, d.wg, d.wu, d.wd, k=cfg.k, aux=True)
+    torch.cuda.synchronize()
+    sample = np.sort(np.random.default_rng(2).choice(cfg.T, 256, replace=False))
+    # the oracle gets every token's routing; its FFN runs on the sample
+    sample = np.concatenate([sample, [cfg.T - 1]]) if sample[-1] != cfg.T - 1 else sample
+    res = oracle.layer_forward(host_array(d.x), cfg.act, host_array(d.wr), host_array(d.wg),
+                               host_array(d.wu), host_array(d.wd), cfg.wdt, k=cfg.k,
+                               tokens=sample)
+    diff = check_routing(host_array(ax["topk_idx"]), host_array(ax["topk_w"]), res.routing)
+    keep = ~diff[sample]
+    if not diff.any():
+        assert np.array_equal(host_array(ax["counts"]), res.disp.counts)
+        assert np.array_equal(host_array(ax["offsets"]), res.disp.offsets)
+    check_close(out_as_f64(out)[sample][keep], res.out[keep], cfg.act, "x over 2 GiB")
+    del d, out, ax
+    torch.cuda.empty_cache()
