@@ -243,15 +243,16 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles("gateup_decode", cfg.name),
-                "kernel": "gateup_decode_kernel<bf16>" if cfg.wdt != "i8" else
-                          "gateup_decode_kernel<i8>",
+                "kernel": "gateup_decode_kernel (bf16 weights)" if cfg.wdt != "i8" else
+                          "gateup_decode_kernel (int8 weights)",
                 "algorithmic_bytes": int(gu_bytes), "mean_ms": round(gu_ms, 4)}
     else:
         achieved = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic_from_profiles("gateup_tiled", cfg.name),
-                "kernel": "ffn_tiled_kernel<gateup>", "algorithmic_flops": gu_flops,
+                "kernel": "ffn_mfma_kernel gate/up (%s weights)" % cfg.wdt,
+                "algorithmic_flops": gu_flops,
                 "mean_ms": round(gu_ms, 4)}
 
     layer_flops = 6.0 * H * F * n_kept

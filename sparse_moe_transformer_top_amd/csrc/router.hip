@@ -12,9 +12,8 @@
 // long one. Lanes split a wave's quarter into 8-element chunks (16-byte loads
 // of bf16 x, 32 bytes of the float32 router row per expert); each router
 // chunk is loaded once and reused for all the block's tokens. Partial dot
-// products are reduced across the 64 lanes with an xor butterfly (fixed
-// order, identical on every lane) and then across the 4 waves through LDS in
-// wave order, so logits are deterministic.
+// products are reduced across the block's 256 lanes through LDS in a fixed
+// order, so logits are deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -82,13 +81,27 @@ MOE_DEV void select_topk(const float (&l)[EC], int E, int k, int64_t t, int32_t*
   }
 }
 
+// Cross-lane reduction through LDS: every lane stores its kTokPerBlock*EC
+// partial sums as one 256-value row per (token, expert), in 8 segments of 32
+// (one pad float per segment so that the 64 lanes of the second pass, which
+// read 8 rows x 8 segments, hit 64 distinct banks). Pass 2 sums each segment
+// in lane order, pass 3 the 8 segment sums: a fixed order, so logits are
+// deterministic, and little code (the kernel runs once per wave at decode
+// sizes, where instruction fetch dominates).
+constexpr int kLanes = kWaves * 64;          // 256 partial sums per (token, expert)
+constexpr int kSeg = 8, kSegLen = kLanes / kSeg, kSegStride = kSegLen + 1;
+constexpr int kRowStride = kSeg * kSegStride;
+
 template <int EC, int ACT>
 __global__ __launch_bounds__(kWaves * 64) void router_topk_kernel(
     const void* __restrict__ x, const float* __restrict__ wr, int64_t T, int H, int E, int k,
     int32_t* __restrict__ idx, float* __restrict__ w, float* __restrict__ logits) {
-  __shared__ float part[kWaves][kTokPerBlock][EC];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int NV = kTokPerBlock * EC;
+  __shared__ float red[NV * kRowStride];
+  __shared__ float seg[NV][kSeg];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * kTokPerBlock;
 
   float acc[kTokPerBlock][EC];
@@ -97,64 +110,66 @@ __global__ __launch_bounds__(kWaves * 64) void router_topk_kernel(
 #pragma unroll
     for (int e = 0; e < EC; ++e) acc[i][e] = 0.f;
 
-  // this wave's quarter of the hidden dimension, in 8-element chunks
+  // this wave's quarter of the hidden dimension, in 8-element chunks. The
+  // loads of a chunk carry no conditions (token and expert indices are
+  // clamped; results for tokens past T and experts past E are never used).
   const int chunks = H / 8;
   const int c_begin = (chunks * wave) / kWaves, c_end = (chunks * (wave + 1)) / kWaves;
-#pragma unroll 2
+  int64_t trow[kTokPerBlock];
+#pragma unroll
+  for (int tt = 0; tt < kTokPerBlock; ++tt) trow[tt] = min(t0 + tt, T - 1);
   for (int c = c_begin + lane; c < c_end; c += 64) {
     const int h0 = c * 8;
-    float wv[EC][8];
+    float xv[kTokPerBlock][8];
 #pragma unroll
-    for (int e = 0; e < EC; ++e) {
-      if (e < E) {
-        const float4* p = reinterpret_cast<const float4*>(wr + (int64_t)e * H + h0);
+    for (int tt = 0; tt < kTokPerBlock; ++tt) load_x8<ACT>(x, trow[tt], H, h0, xv[tt]);
+#pragma unroll
+    for (int e0 = 0; e0 < EC; e0 += 8) {
+      float wv[8][8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4* p = reinterpret_cast<const float4*>(wr + (int64_t)min(e0 + e, E - 1) * H + h0);
         const float4 a = p[0], b = p[1];
         wv[e][0] = a.x; wv[e][1] = a.y; wv[e][2] = a.z; wv[e][3] = a.w;
         wv[e][4] = b.x; wv[e][5] = b.y; wv[e][6] = b.z; wv[e][7] = b.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wv[e][i] = 0.f;
       }
-    }
 #pragma unroll
-    for (int tt = 0; tt < kTokPerBlock; ++tt) {
-      const int64_t t = t0 + tt;
-      if (t < T) {
-        float xv[8];
-        load_x8<ACT>(x, t, H, h0, xv);
+      for (int tt = 0; tt < kTokPerBlock; ++tt)
 #pragma unroll
-        for (int e = 0; e < EC; ++e)
+        for (int e = 0; e < 8; ++e)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[tt][e] = fmaf(xv[i], wv[e][i], acc[tt][e]);
-      }
+          for (int i = 0; i < 8; ++i)
+            acc[tt][e0 + e] = fmaf(xv[tt][i], wv[e][i], acc[tt][e0 + e]);
     }
   }
 
+  // pass 1: lane tid's partial sums go to position tid of every row
+  const int pos = (tid / kSegLen) * kSegStride + tid % kSegLen;
 #pragma unroll
   for (int tt = 0; tt < kTokPerBlock; ++tt)
 #pragma unroll
-    for (int e = 0; e < EC; ++e) acc[tt][e] = wave_sum_xor(acc[tt][e]);
-  if (lane == 0) {
-#pragma unroll
-    for (int tt = 0; tt < kTokPerBlock; ++tt)
-#pragma unroll
-      for (int e = 0; e < EC; ++e) part[wave][tt][e] = acc[tt][e];
+    for (int e = 0; e < EC; ++e) red[(tt * EC + e) * kRowStride + pos] = acc[tt][e];
+  __syncthreads();
+  // pass 2: segment sums, in lane order
+  for (int j = tid; j < NV * kSeg; j += kLanes) {
+    const float* r = red + (j / kSeg) * kRowStride + (j % kSeg) * kSegStride;
+    float v = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < kSegLen; ++i) v += r[i];
+    seg[j / kSeg][j % kSeg] = v;
   }
   __syncthreads();
-  if (wave != 0) return;
+  // pass 3: one lane per token adds its segment sums and selects
+  if (tid < kTokPerBlock && t0 + tid < T) {
+    float l[EC];
 #pragma unroll
-  for (int tt = 0; tt < kTokPerBlock; ++tt) {
-    if (lane == tt && t0 + tt < T) {
-      float l[EC];
+    for (int e = 0; e < EC; ++e) {
+      float v = 0.f;
 #pragma unroll
-      for (int e = 0; e < EC; ++e) {
-        float v = part[0][tt][e];
-#pragma unroll
-        for (int wv = 1; wv < kWaves; ++wv) v += part[wv][tt][e];
-        l[e] = v;
-      }
-      select_topk<EC>(l, E, k, t0 + tt, idx, w, logits);
+      for (int q = 0; q < kSeg; ++q) v += seg[tid * EC + e][q];
+      l[e] = v;
     }
+    select_topk<EC>(l, E, k, t0 + tid, idx, w, logits);
   }
 }
 
