@@ -299,3 +299,40 @@ def expert_utilization(idx: np.ndarray, E: int) -> np.ndarray:
     idx = np.asarray(idx)
     counts = np.bincount(idx.ravel(), minlength=E).astype(np.float64)
     return counts / idx.size * E
+
+
+@dataclass
+class RoutingStats:
+    margin: np.ndarray           # [T] l_(k) - l_(k+1); +inf when k == E
+    unselected_mass: np.ndarray  # [T] full-softmax probability outside the top k
+    utilization: np.ndarray      # [E] counts / (T*k) * E
+
+
+def routing_stats(l32: np.ndarray, k: int, counts: np.ndarray) -> RoutingStats:
+    """Routing statistics the page discusses after training (section
+    "Routing: top-2 without auxiliary loss", the utilisation analysis and the
+    remark that a clear top-2 usually stands apart from the 3rd expert, while
+    the 3rd and 4th still carry noticeable probability).
+
+    Per token: the margin between the last selected logit and the best
+    unselected one, l_(k) - l_(k+1) (values in descending order; the order of
+    equal values does not matter here), and the probability a softmax over
+    all E logits gives to the experts outside the top k. Per expert: the
+    picks counted by the dispatch, normalised as in expert_utilization. All in
+    float64 from the float32 logits."""
+    l = np.asarray(l32, np.float32).astype(np.float64)
+    T, E = l.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    ranked = -np.sort(-l, axis=1)
+    margin = ranked[:, k - 1] - ranked[:, k] if k < E else np.full(T, np.inf)
+    z = np.exp(l - ranked[:, :1])
+    # the selected set: k largest, lower index first among equal values
+    order = np.argsort(-np.asarray(l32, np.float32), axis=1, kind="stable")
+    outside = np.ones_like(z, bool)
+    np.put_along_axis(outside, order[:, :k], False, axis=1)
+    mass = (z * outside).sum(axis=1) / z.sum(axis=1) if T else np.zeros(0)
+    counts = np.asarray(counts, np.float64)
+    util = counts * E / (T * k) if T else np.zeros(E)
+    return RoutingStats(margin, mass, util)
+

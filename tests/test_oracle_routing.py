@@ -126,3 +126,82 @@ def test_uniform_routing_statistics_tiny_config():
     util = oracle.expert_utilization(r.idx, 8)
     assert np.all(np.abs(util - 1.0) < 0.3)
     assert abs(util.mean() - 1.0) < 1e-12
+
+
+# --- routing statistics (the page's post-training utilisation analysis and
+# its remark on the gap to the 3rd expert) ---------------------------------
+
+def test_routing_stats_hand_cases():
+    l = np.array([[5.0, 1.0, 2.0, 0.0]], np.float32)
+    c = np.zeros(4)
+    assert oracle.routing_stats(l, 1, c).margin[0] == 3.0
+    assert oracle.routing_stats(l, 2, c).margin[0] == 1.0
+    assert oracle.routing_stats(l, 3, c).margin[0] == 1.0
+    assert oracle.routing_stats(l, 4, c).margin[0] == np.inf
+    assert oracle.routing_stats(l, 4, c).unselected_mass[0] == 0.0
+    # ln 3 against three zeros, top-1: 3 / (3 + 3) outside-mass 1/2
+    l = np.array([[math.log(3.0), 0.0, 0.0, 0.0]], np.float32)
+    m = oracle.routing_stats(l, 1, c).unselected_mass[0]
+    assert abs(m - 3.0 / (float(np.float32(3.0)) + 3.0)) < 1e-7
+    # all equal: (E - k) / E outside the selection, margin 0 (tie at the boundary)
+    r = oracle.routing_stats(np.zeros((3, 8), np.float32), 2, np.zeros(8))
+    assert np.all(r.unselected_mass == 0.75) and np.all(r.margin == 0.0)
+
+
+def test_routing_stats_two_level_closed_form():
+    # k selected logits at a, E - k at b: outside mass (E-k) e^b / (k e^a + (E-k) e^b)
+    for E, k, a, b in ((8, 2, 1.5, -0.25), (16, 4, 0.0, -3.0), (4, 1, 2.0, 2.0 - 1e-3)):
+        l = np.full((1, E), b, np.float32)
+        l[0, :k] = a
+        r = oracle.routing_stats(l, k, np.zeros(E))
+        a64, b64 = float(np.float32(a)), float(np.float32(b))
+        want = (E - k) * math.exp(b64) / (k * math.exp(a64) + (E - k) * math.exp(b64))
+        assert abs(r.unselected_mass[0] - want) < 1e-12
+        assert r.margin[0] == a64 - b64
+
+
+def test_routing_stats_brute_force():
+    rng = np.random.default_rng(12)
+    for E in (4, 8, 16):
+        for k in range(1, min(E, 4) + 1):
+            # integer logits force ties, including at the k / k+1 boundary
+            l = np.where(rng.random((40, E)) < 0.5, rng.integers(-2, 3, (40, E)),
+                         rng.standard_normal((40, E))).astype(np.float32)
+            r = oracle.routing_stats(l, k, np.zeros(E))
+            for t in range(40):
+                ranked = sorted(((-float(v), i) for i, v in enumerate(l[t])))
+                chosen = {i for _, i in ranked[:k]}
+                vals = [-nv for nv, _ in ranked]
+                want_m = vals[k - 1] - vals[k] if k < E else math.inf
+                assert r.margin[t] == want_m
+                zs = [math.exp(float(v) - vals[0]) for v in l[t]]
+                want = sum(z for i, z in enumerate(zs) if i not in chosen) / sum(zs)
+                assert abs(r.unselected_mass[t] - want) < 1e-12
+
+
+def test_selected_weights_match_unselected_mass():
+    # the softmax over the k selected logits is the full softmax renormalised
+    # by what the selection holds: w_j = p_j / (1 - outside mass)
+    rng = np.random.default_rng(5)
+    l32 = rng.standard_normal((30, 8)).astype(np.float32)
+    for k in (1, 2, 3):
+        ro = oracle.top_k_softmax(l32, l32.astype(np.float64), k)
+        st = oracle.routing_stats(l32, k, np.zeros(8))
+        l = l32.astype(np.float64)
+        p = np.exp(l - l.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        psel = np.take_along_axis(p, ro.idx.astype(np.int64), axis=1)
+        assert np.allclose(ro.w * (1.0 - st.unselected_mass)[:, None], psel, rtol=0, atol=1e-14)
+
+
+def test_utilization_from_dispatch_counts():
+    # the dispatch's sequential counts give the same utilisation as a bincount
+    # of the indices; it sums to E
+    rng = np.random.default_rng(8)
+    for E, k, T in ((8, 2, 500), (16, 4, 97), (4, 1, 33)):
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        counts = oracle.dispatch(idx, E, None).counts
+        r = oracle.routing_stats(np.zeros((T, E), np.float32), k, counts)
+        assert np.array_equal(r.utilization, oracle.expert_utilization(idx, E))
+        assert abs(r.utilization.sum() - E) < 1e-12
+    assert np.all(oracle.routing_stats(np.zeros((0, 8), np.float32), 2, np.zeros(8)).utilization == 0)
