@@ -139,6 +139,27 @@ class Layer:
         return gu_ms, sum(dn) / steps, disp
 
 
+    def routing_stats_time(self, reps=50):
+        """Mean duration of moe_routing_stats on this workload's router
+        logits and dispatch counts. The launches are queued behind a ~1 ms
+        device-side delay (torch.cuda._sleep), so the events bracket
+        back-to-back kernels rather than the host's launch latency."""
+        torch, d, c, m = self.torch, self.d, self.cfg, self.moe
+        idx, _, logits = m.moe_router_topk(d.x, d.wr, c.k, return_logits=True)
+        counts = m.moe_dispatch(idx, c.E, c.capacity_factor)["counts"]
+        for _ in range(3):
+            m.moe_routing_stats(logits, counts, c.k)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(2_000_000)
+        a.record()
+        for _ in range(reps):
+            m.moe_routing_stats(logits, counts, c.k)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+
 def cpu_baseline(layer, n_tokens):
     """The oracle on the first n_tokens tokens of the workload (routing and
     dispatch over all T tokens, expert FFN and combine for the sample)."""
@@ -271,6 +292,14 @@ def main():
                   "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                   "stages_ms": {"gate_up": round(gu_ms, 4), "down": round(dn_ms, 4)}},
     }
+
+    # routing statistics (per-token margin and outside-top-k mass, per-expert
+    # utilisation): reads the T x E float32 logits and the counts, writes 8
+    # bytes per token and 4 per expert
+    rs_ms = layer.routing_stats_time()
+    rs_bytes = cfg.T * cfg.E * 4 + cfg.T * 8 + cfg.E * 8
+    result["routing_stats"] = {"us": round(rs_ms * 1e3, 2), "bytes": rs_bytes,
+                               "GBps": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1)}
 
     if not args.no_prefill and cfg.name == "decode":
         pcfg = synth.CONFIGS["prefill"]

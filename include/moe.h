@@ -202,6 +202,29 @@ moe_status moe_combine(const void* y_perm, const int32_t* slot_row, const float*
                        moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Routing statistics. Page: section "Routing: top-2 without auxiliary loss"
+ * (the post-training expert-utilisation analysis, normalised so that a
+ * balanced router scores 1.0 per expert as the page's comment intends, and
+ * the remark that a clear top-2 usually stands apart from the 3rd expert
+ * while the 3rd and 4th still carry noticeable probability).
+ *
+ * logits [T,E] float32 (in; e.g. moe_router_topk's logits output),
+ * counts [E] int32 (in; moe_dispatch's counts: picks per expert before any
+ * capacity drop). Outputs, each may be NULL (then not computed):
+ *   utilization [E] float32: counts[e] * E / (T*k), 0 when T == 0;
+ *   margin [T] float32: l_(k) - l_(k+1), the last selected logit minus the
+ *     best unselected one (descending order; +inf when k == E);
+ *   unselected_mass [T] float32: the probability a softmax over all E
+ *     logits gives to the experts outside the top k (lower index first
+ *     among equal logits; the value does not depend on that order).
+ * logits may be NULL when margin and unselected_mass are; counts when
+ * utilization is. Float32 arithmetic, deterministic.
+ * ------------------------------------------------------------------------ */
+moe_status moe_routing_stats(const float* logits, const int32_t* counts, int64_t T, int32_t E,
+                             int32_t k, float* utilization, float* margin,
+                             float* unselected_mass, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * The whole layer: router_topk -> dispatch -> expert_ffn -> combine on one
  * stream, with no host synchronisation. Page: GrokMoELayer.forward.
  *

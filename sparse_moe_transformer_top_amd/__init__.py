@@ -14,5 +14,6 @@ from .api import (  # noqa: F401
     moe_expert_gate_up,
     moe_layer_forward,
     moe_router_topk,
+    moe_routing_stats,
 )
 from ._lib import MoeError, LIB_PATH, load as load_library  # noqa: F401

@@ -38,6 +38,7 @@ SIGNATURES = {
     "moe_expert_down": (C.c_int, [_P, C.c_int, _P, _I64, _I32, _I32, _I32, _I32, _P, C.c_int,
                                   _P, _P, _P, _SZ, _P]),
     "moe_combine": (C.c_int, [_P, _P, _P, _I64, _I32, _I32, C.c_int, _P, _P]),
+    "moe_routing_stats": (C.c_int, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P]),
     "moe_layer_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, C.c_int, C.c_int]),
     "moe_layer_forward": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _P, _P, _P, _I64, _I32,
                                     _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),

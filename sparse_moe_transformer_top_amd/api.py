@@ -141,6 +141,21 @@ def moe_combine(y_perm: torch.Tensor, slot_row: torch.Tensor, topk_w: torch.Tens
     return out
 
 
+def moe_routing_stats(logits: torch.Tensor, counts: torch.Tensor, k: int):
+    """dict(utilization [E], margin [T], unselected_mass [T]) float32 from
+    logits [T,E] float32 and the dispatch counts [E] int32."""
+    _need(logits, "logits", torch.float32, 2)
+    _need(counts, "counts", torch.int32, 1)
+    T, E = logits.shape
+    f32 = dict(dtype=torch.float32, device=logits.device)
+    out = dict(utilization=torch.empty(E, **f32), margin=torch.empty(T, **f32),
+               unselected_mass=torch.empty(T, **f32))
+    check(_lib.load().moe_routing_stats(_p(logits), _p(counts), T, E, k, _p(out["utilization"]),
+                                        _p(out["margin"]), _p(out["unselected_mass"]),
+                                        _stream(logits.device)))
+    return out
+
+
 def layer_workspace_bytes(T: int, H: int, F: int, E: int, k: int, act: torch.dtype,
                           wdt: torch.dtype) -> int:
     return _lib.load().moe_layer_workspace_bytes(T, H, F, E, k, _DT[act], _DT[wdt])

@@ -325,6 +325,24 @@ moe_status moe_combine(const void* y_perm, const int32_t* slot_row, const float*
                     "combine launch");
 }
 
+moe_status moe_routing_stats(const float* logits, const int32_t* counts, int64_t T, int32_t E,
+                             int32_t k, float* utilization, float* margin,
+                             float* unselected_mass, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_shape(T, E, k))) return st;
+  const bool per_token = (margin || unselected_mass) && T > 0;
+  if (!utilization && !per_token) return ok();
+  REQUIRE(!utilization || counts, MOE_ERR_INVALID_ARGUMENT,
+          "counts must be non-NULL when utilization is requested");
+  REQUIRE(!per_token || logits, MOE_ERR_INVALID_ARGUMENT,
+          "logits must be non-NULL when margin or unselected_mass is requested");
+  return hip_status(launch_routing_stats(logits, counts, T, E, k, utilization,
+                                         per_token ? margin : nullptr,
+                                         per_token ? unselected_mass : nullptr,
+                                         (hipStream_t)stream),
+                    "routing statistics launch");
+}
+
 size_t moe_layer_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                                  moe_dtype act_dtype, moe_dtype w_dtype) {
   if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1) return 0;

@@ -59,4 +59,8 @@ size_t decode_ws_bytes(int64_t T, int H, int k);
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 
+// routing statistics (stats.hip)
+hipError_t launch_routing_stats(const float* logits, const int32_t* counts, int64_t T, int E,
+                                int k, float* util, float* margin, float* mass, hipStream_t s);
+
 }  // namespace moe

@@ -126,3 +126,14 @@ def generate_host(cfg: LayerConfig, seed: Optional[int] = None) -> HostInputs:
             wr[e] = (wr[e] + f32(a) * u).astype(f32)
 
     return HostInputs(cfg, x, wr, wg, wu, wd, sg, su, sd)
+
+
+def routing_logits(T: int, E: int, seed: int, tie_frac: float = 0.3) -> np.ndarray:
+    """Seeded float32 logits [T,E]: N(0,1) draws with a fraction of entries
+    replaced by small integers, so that equal values (also at the k / k+1
+    boundary) occur."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((T, E))
+    ints = rng.integers(-2, 3, (T, E)).astype(np.float64)
+    return np.where(rng.random((T, E)) < tie_frac, ints, g).astype(np.float32)
+

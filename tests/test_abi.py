@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -114,6 +114,19 @@ def test_stage_entry_points_argument_errors(lib):
     assert dn(wdt=I8) == INV
     assert dn(sd=P) == INV
     assert dn(F=200) == UNS
+
+
+def test_routing_stats_argument_errors(lib):
+    st = lib.moe_routing_stats
+    assert st(P, P, 8, 8, 2, None, None, None, None) == OK          # nothing requested
+    assert st(None, P, 0, 8, 2, None, P, P, None) == OK             # T = 0: nothing per token
+    assert st(P, None, 8, 8, 2, P, None, None, None) == INV         # utilisation needs counts
+    assert st(None, P, 8, 8, 2, None, P, None, None) == INV         # margin needs logits
+    assert st(P, P, 8, 8, 0, None, P, None, None) == INV
+    assert st(P, P, 8, 8, 9, None, P, None, None) == INV
+    assert st(P, P, 8, 17, 2, None, P, None, None) == UNS
+    assert st(P, P, 8, 8, 5, None, P, None, None) == UNS
+    assert st(P, P, -1, 8, 2, None, P, None, None) == INV
 
 
 def test_combine_argument_errors(lib):
