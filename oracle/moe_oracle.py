@@ -38,8 +38,26 @@ def widen_bf16_bits(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+INT4_K_PER_SCALE = 128
+
+
+def widen_int4(packed: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Packed int4 rows [..., K/2] (byte j: k = 2j in the low nibble, k = 2j+1
+    in the high nibble; each nibble an unsigned code u, value u - 8) with one
+    scale per 128 consecutive k ([..., K/128]) -> float64 [..., K]."""
+    p = np.asarray(packed, np.uint8)
+    codes = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.float64)
+    codes[..., 0::2] = (p & 0x0F).astype(np.float64)
+    codes[..., 1::2] = (p >> 4).astype(np.float64)
+    s = np.repeat(np.asarray(scale, np.float32).astype(np.float64), INT4_K_PER_SCALE, axis=-1)
+    if s.shape != codes.shape:
+        raise ValueError("int4 scales must hold one value per row and 128 k")
+    return (codes - 8.0) * s
+
+
 def widen(a: np.ndarray, kind: str, scale: Optional[np.ndarray] = None) -> np.ndarray:
-    """Stored matrix -> float64. kind: 'f32' | 'bf16' | 'i8' (rows scaled by scale[row])."""
+    """Stored matrix -> float64. kind: 'f32' | 'bf16' | 'i8' (rows scaled by
+    scale[row]) | 'i4' (packed nibbles, scale per row and 128 k)."""
     if kind == "f32":
         return np.asarray(a, np.float32).astype(np.float64)
     if kind == "bf16":
@@ -50,6 +68,10 @@ def widen(a: np.ndarray, kind: str, scale: Optional[np.ndarray] = None) -> np.nd
         # q * s is exact in float64 (8-bit times 24-bit significands)
         return np.asarray(a, np.int8).astype(np.float64) * \
             np.asarray(scale, np.float32).astype(np.float64)[:, None]
+    if kind == "i4":
+        if scale is None:
+            raise ValueError("int4 weights need their group scales")
+        return widen_int4(a, scale)
     raise ValueError(kind)
 
 

@@ -19,4 +19,6 @@ from .gen import (  # noqa: F401
     bf16_bits_from_f32,
     f32_from_bf16_bits,
     quantize_int8_rows,
+    quantize_int4_groups,
+    INT4_GROUP,
 )

@@ -23,7 +23,7 @@ class LayerConfig:
     k: int = 2                  # experts per token
     capacity_factor: Optional[float] = None   # None: no capacity limit
     act: str = "bf16"           # activation storage dtype: "f32" | "bf16"
-    wdt: str = "bf16"           # expert weight storage dtype: "f32" | "bf16" | "i8"
+    wdt: str = "bf16"           # expert weight storage dtype: "f32" | "bf16" | "i8" | "i4"
     # Router skew: row e of the router weight gets skew[e] * u added, with u
     # the unit vector along the mean of the (stored) token activations.
     skew: Tuple[float, ...] = field(default_factory=tuple)
@@ -39,6 +39,8 @@ class LayerConfig:
 
     def expert_weight_bytes(self) -> int:
         """Bytes of one expert's three matrices at the storage dtype."""
+        if self.wdt == "i4":   # packed nibbles + one float32 scale per 128 k
+            return 3 * self.H * self.F // 2 + 3 * self.H * self.F // 128 * 4
         per = {"f32": 4, "bf16": 2, "i8": 1}[self.wdt]
         return 3 * self.H * self.F * per
 
@@ -67,6 +69,10 @@ CONFIGS = {
         "capacity", T=16384, H=6144, F=32768, capacity_factor=1.25,
         wdt="i8", skew=SKEW_T16384,
         description="capacity 1.25, int8 weights with per-row fp32 scales, skewed router, T=16384"),
+    "decode_i4": LayerConfig(
+        "decode_i4", T=8, H=6144, F=32768, wdt="i4",
+        description="Grok-1 shape decode with int4 weights (one fp32 scale per row and 128 k): "
+                    "T=8, bf16 activations, no drop"),
 }
 
 # Sizes small enough for an element-by-element comparison with the oracle
@@ -85,6 +91,9 @@ PARITY_CONFIGS = {
     "p_bf16_tail": LayerConfig("p_bf16_tail", T=150, H=320, F=448, seed=10),
     "p_i8_dec": LayerConfig("p_i8_dec", T=9, H=512, F=1024, wdt="i8", seed=11),
     "p_dec1": LayerConfig("p_dec1", T=1, H=384, F=640, seed=12),
+    "p_i4_dec": LayerConfig("p_i4_dec", T=9, H=512, F=1024, wdt="i4", seed=13),
+    "p_i4_dec16": LayerConfig("p_i4_dec16", T=16, H=640, F=384, wdt="i4", seed=14),
+    "p_i4_dec1": LayerConfig("p_i4_dec1", T=1, H=384, F=640, wdt="i4", seed=15),
 }
 
 

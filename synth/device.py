@@ -40,6 +40,17 @@ def quantize_int8_rows_t(w: torch.Tensor):
     return q, s
 
 
+def quantize_int4_groups_t(w: torch.Tensor, group: int = 128):
+    """Group-wise symmetric int4 (same rule as synth.gen.quantize_int4_groups):
+    packed unsigned nibbles q + 8, k even in the low nibble; scales [N, K/group]."""
+    N, K = w.shape
+    g = w.view(N, K // group, group)
+    s = g.abs().amax(dim=2) / 7.0
+    s_safe = torch.where(s > 0, s, torch.ones_like(s))
+    u = (torch.round(g / s_safe[:, :, None]).clamp_(-7, 7) + 8).to(torch.uint8).view(N, K)
+    return u[:, 0::2] | (u[:, 1::2] << 4), s
+
+
 @dataclass
 class DeviceInputs:
     cfg: LayerConfig
@@ -60,6 +71,8 @@ def _store(w32: torch.Tensor, wdt: str):
         return w32.to(torch.bfloat16), None
     if wdt == "i8":
         return quantize_int8_rows_t(w32)
+    if wdt == "i4":
+        return quantize_int4_groups_t(w32)
     raise ValueError(wdt)
 
 
@@ -79,15 +92,19 @@ def generate_device(cfg: LayerConfig, device="cuda", seed: Optional[int] = None,
     if x_only:
         return DeviceInputs(cfg, x, wr, None, None, None)
 
-    wt = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[cfg.wdt]
-    wg = torch.empty((E, F, H), dtype=wt, device=device)
-    wu = torch.empty((E, F, H), dtype=wt, device=device)
-    wd = torch.empty((E, H, F), dtype=wt, device=device)
+    wt = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8,
+          "i4": torch.uint8}[cfg.wdt]
+    half = 2 if cfg.wdt == "i4" else 1
+    wg = torch.empty((E, F, H // half), dtype=wt, device=device)
+    wu = torch.empty((E, F, H // half), dtype=wt, device=device)
+    wd = torch.empty((E, H, F // half), dtype=wt, device=device)
     sg = su = sd = None
+    f32 = dict(dtype=torch.float32, device=device)
     if cfg.wdt == "i8":
-        sg = torch.empty((E, F), dtype=torch.float32, device=device)
-        su = torch.empty((E, F), dtype=torch.float32, device=device)
-        sd = torch.empty((E, H), dtype=torch.float32, device=device)
+        sg, su, sd = torch.empty((E, F), **f32), torch.empty((E, F), **f32), torch.empty((E, H), **f32)
+    if cfg.wdt == "i4":
+        sg, su = torch.empty((E, F, H // 128), **f32), torch.empty((E, F, H // 128), **f32)
+        sd = torch.empty((E, H, F // 128), **f32)
     for e in range(E):
         for j, (dst, shape, std, sdst) in enumerate((
                 (wg, (F, H), H ** -0.5, sg),

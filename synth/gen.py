@@ -45,14 +45,37 @@ def quantize_int8_rows(w: np.ndarray):
     return q, s
 
 
+INT4_GROUP = 128   # k values sharing one int4 scale
+
+
+def quantize_int4_groups(w: np.ndarray):
+    """Symmetric int4 quantisation of a float32 matrix [N, K] with one scale
+    per row and group of 128 consecutive k: s = max|w| / 7 over the group,
+    q = clip(rint(w / s), -7, 7). Stored as unsigned nibbles u = q + 8, two
+    per byte (k even in the low nibble).
+
+    Returns (packed uint8 [N, K/2], s float32 [N, K/128]) with
+    w ~= (u - 8) * s."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    g = w.reshape(N, K // INT4_GROUP, INT4_GROUP)
+    s = (np.max(np.abs(g), axis=2) / np.float32(7.0)).astype(np.float32)
+    s_safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(g / s_safe[:, :, None]), -7, 7).astype(np.int16).reshape(N, K)
+    u = (q + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).astype(np.uint8), s
+
+
 @dataclass
 class HostInputs:
     """Arrays of one layer instance as the layer stores them.
 
     x   : float32 [T,H] (act f32) or uint16 bf16 bits [T,H] (act bf16)
     wr  : float32 [E,H]
-    wg, wu : [E,F,H]; wd : [E,H,F]  -- float32, uint16 bf16 bits, or int8
-    sg, su : float32 [E,F]; sd : float32 [E,H]  -- only for int8 weights
+    wg, wu : [E,F,H]; wd : [E,H,F]  -- float32, uint16 bf16 bits, or int8;
+             int4: packed uint8 [E,F,H/2] and [E,H,F/2]
+    sg, su : float32 [E,F]; sd : float32 [E,H]  -- int8 row scales; int4:
+             [E,F,H/128] and [E,H,F/128] group scales
     """
     cfg: LayerConfig
     x: np.ndarray
@@ -78,6 +101,8 @@ def _store_weight(w32: np.ndarray, wdt: str):
         return bf16_bits_from_f32(w32), None
     if wdt == "i8":
         return quantize_int8_rows(w32)
+    if wdt == "i4":
+        return quantize_int4_groups(w32)
     raise ValueError(wdt)
 
 
@@ -101,15 +126,20 @@ def generate_host(cfg: LayerConfig, seed: Optional[int] = None) -> HostInputs:
     wr = (rng.standard_normal((E, H), dtype=f32) * f32(1.0 / np.sqrt(H))).astype(f32)
     x = bf16_bits_from_f32(x32) if cfg.act == "bf16" else x32
 
-    wdt_np = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[cfg.wdt]
-    wg = np.empty((E, F, H), wdt_np)
-    wu = np.empty((E, F, H), wdt_np)
-    wd = np.empty((E, H, F), wdt_np)
+    wdt_np = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "i4": np.uint8}[cfg.wdt]
+    half = 2 if cfg.wdt == "i4" else 1
+    wg = np.empty((E, F, H // half), wdt_np)
+    wu = np.empty((E, F, H // half), wdt_np)
+    wd = np.empty((E, H, F // half), wdt_np)
     sg = su = sd = None
     if cfg.wdt == "i8":
         sg = np.empty((E, F), f32)
         su = np.empty((E, F), f32)
         sd = np.empty((E, H), f32)
+    if cfg.wdt == "i4":
+        sg = np.empty((E, F, H // INT4_GROUP), f32)
+        su = np.empty((E, F, H // INT4_GROUP), f32)
+        sd = np.empty((E, H, F // INT4_GROUP), f32)
     for e in range(E):
         g = rng.standard_normal((F, H), dtype=f32) * f32(1.0 / np.sqrt(H))
         u = rng.standard_normal((F, H), dtype=f32) * f32(1.0 / np.sqrt(H))
@@ -117,7 +147,7 @@ def generate_host(cfg: LayerConfig, seed: Optional[int] = None) -> HostInputs:
         wg[e], s0 = _store_weight(g.astype(f32), cfg.wdt)
         wu[e], s1 = _store_weight(u.astype(f32), cfg.wdt)
         wd[e], s2 = _store_weight(d.astype(f32), cfg.wdt)
-        if cfg.wdt == "i8":
+        if cfg.wdt in ("i8", "i4"):
             sg[e], su[e], sd[e] = s0, s1, s2
 
     if cfg.skew:

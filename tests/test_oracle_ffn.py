@@ -38,7 +38,7 @@ def _dense_masked_reference(inp, cfg, res):
     return out.numpy()
 
 
-@pytest.mark.parametrize("name", ["tiny", "p_cap", "p_i8", "p_cap_i8"])
+@pytest.mark.parametrize("name", ["tiny", "p_cap", "p_i8", "p_cap_i8", "p_i4_dec"])
 def test_dense_masked_brute_force(name):
     cfg = synth.get_config(name)
     if cfg.T * cfg.H * cfg.F > 80_000_000:
@@ -153,6 +153,44 @@ def test_widen_int8_and_bf16():
     t = torch.randn(1000).to(torch.bfloat16)
     bits = t.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle.widen(bits, "bf16"), t.to(torch.float64).numpy())
+
+
+def test_widen_int4_hand_packed():
+    # one row of K = 256 (two scale groups). Byte j holds k = 2j (low nibble)
+    # and k = 2j+1 (high nibble); a nibble u means u - 8.
+    packed = np.full((1, 128), 0x88, np.uint8)          # every code 8: value 0
+    packed[0, 0] = 0x8F        # k0 = 15-8 = 7,  k1 = 8-8 = 0
+    packed[0, 1] = 0x18        # k2 = 8-8 = 0,   k3 = 1-8 = -7
+    packed[0, 63] = 0xF1       # k126 = -7,      k127 = 7
+    packed[0, 64] = 0x9C       # k128 = 12-8 = 4, k129 = 9-8 = 1 (second group)
+    packed[0, 127] = 0x08      # k254 = 0,       k255 = -8 (code 0)
+    s = np.array([[0.5, 3.0]], np.float32)
+    w = oracle.widen(packed, "i4", s)
+    assert w.shape == (1, 256)
+    want = np.zeros(256)
+    want[[0, 3, 126, 127, 128, 129, 255]] = [3.5, -3.5, -3.5, 3.5, 12.0, 3.0, -24.0]
+    assert np.array_equal(w[0], want)
+
+
+def test_int4_quantisation_round_trip():
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((5, 384)) * rng.uniform(0.01, 3.0, (5, 1))).astype(np.float32)
+    w[2, 128:256] = 0.0                                  # an all-zero group
+    packed, s = synth.quantize_int4_groups(w)
+    assert packed.shape == (5, 192) and s.shape == (5, 3)
+    back = oracle.widen(packed, "i4", s)
+    g = w.reshape(5, 3, 128).astype(np.float64)
+    err = np.abs(back.reshape(5, 3, 128) - g)
+    # rounding to the nearest multiple of s: at most s/2 (plus float32 rounding of w/s)
+    assert np.all(err <= (s.astype(np.float64) * (0.5 + 1e-6))[:, :, None])
+    # the group's largest |w| maps to +-7 s
+    amax = np.abs(g).argmax(axis=2)
+    top = np.take_along_axis(back.reshape(5, 3, 128), amax[:, :, None], axis=2)[:, :, 0]
+    assert np.array_equal(np.abs(top), 7.0 * s.astype(np.float64))
+    assert np.all(back[2, 128:256] == 0.0) and s[2, 1] == 0.0
+    # codes stay in 1 ... 15 (values -7 ... 7)
+    codes = np.concatenate([packed & 15, packed >> 4])
+    assert codes.min() >= 1 and codes.max() <= 15
 
 
 def test_combine_and_hidden_agree_with_layer():
