@@ -208,7 +208,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "skew", "capacity"])
+                    choices=["decode", "prefill", "skew", "capacity", "decode_i4"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill secondary line")
     ap.add_argument("--cpu-tokens", type=int, default=8,
                     help="tokens in the oracle's timed sample (0 skips the CPU baseline)")
@@ -245,27 +245,29 @@ def main():
     log(f"{cfg.name}: {ms:.4f} ms/step")
     gu_ms, dn_ms, disp = layer.stage_times(args.steps)
     n_touched, n_per_e, n_kept = touched_experts(disp, cfg.E)
-    esz = {"f32": 4, "bf16": 2, "i8": 1}[cfg.wdt]
+    esz = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}[cfg.wdt]
     asz = 2 if cfg.act == "bf16" else 4
     H, F = cfg.H, cfg.F
     decode_like = cfg.T <= 16
 
     # algorithmic work of the gate/up launch: every touched expert's gate and
     # up weights read once (+ scales), the gathered x rows read, h written
-    gu_bytes = n_touched * 2 * F * H * esz + n_kept * (H + F) * asz + \
-        (n_touched * 2 * F * 4 if cfg.wdt == "i8" else 0)
+    # scales: int8 one float32 per weight row, int4 one per row and 128 k
+    gu_scales = {"i8": 2 * F * 4, "i4": 2 * F * (H // 128) * 4}.get(cfg.wdt, 0)
+    dn_scales = {"i8": H * 4, "i4": H * (F // 128) * 4}.get(cfg.wdt, 0)
+    gu_bytes = int(n_touched * 2 * F * H * esz) + n_kept * (H + F) * asz + n_touched * gu_scales
     gu_flops = 4.0 * H * F * n_kept
     # whole layer: every touched expert's three matrices once, x read and out
     # written, h and y_perm each written once and read once
-    layer_bytes = n_touched * 3 * F * H * esz + cfg.T * H * asz * 2 + \
-        n_kept * (H + F) * asz * 2
+    layer_bytes = int(n_touched * 3 * F * H * esz) + cfg.T * H * asz * 2 + \
+        n_kept * (H + F) * asz * 2 + n_touched * (gu_scales + dn_scales)
     if decode_like:
         achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles("gateup_decode", cfg.name),
-                "kernel": "gateup_decode_kernel (bf16 weights)" if cfg.wdt != "i8" else
-                          "gateup_decode_kernel (int8 weights)",
+                "kernel": "gateup_decode_kernel (%s weights)" % {
+                    "bf16": "bf16", "i8": "int8", "i4": "int4"}[cfg.wdt],
                 "algorithmic_bytes": int(gu_bytes), "mean_ms": round(gu_ms, 4)}
     else:
         achieved = gu_flops / (gu_ms * 1e-3) / 1e12
@@ -281,7 +283,8 @@ def main():
         "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.act if cfg.wdt != "i8" else "bf16 (int8 weights)", "data": "synthetic",
+        "dtype": cfg.act if cfg.wdt in ("f32", "bf16") else
+                 "bf16 (%s weights)" % {"i8": "int8", "i4": "int4"}[cfg.wdt], "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "T": cfg.T, "H": H, "F": F,
                    "E": cfg.E, "k": cfg.k, "capacity_factor": cfg.capacity_factor,
                    "weights": cfg.wdt, "experts_touched": n_touched, "rows_per_expert": n_per_e},

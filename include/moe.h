@@ -34,13 +34,22 @@
  *     1 <= E <= 16, 1 <= k <= min(E, 4), 64 <= H, F <= 2^20 with
  *     H % 64 == 0 and F % 64 == 0.
  *   - dtypes: activations (x, h, y_perm, out) are MOE_F32 or MOE_BF16; expert
- *     weights are MOE_F32 (with f32 activations), MOE_BF16 or MOE_I8 (with
- *     bf16 activations). The router weight, routing weights and scales are
- *     always float32; indices are int32.
+ *     weights are MOE_F32 (with f32 activations), MOE_BF16, MOE_I8 or MOE_I4
+ *     (with bf16 activations). The router weight, routing weights and scales
+ *     are always float32; indices are int32.
  *   - Weights follow nn.Linear's [out, in] layout: w_gate, w_up are [E][F][H],
  *     w_down is [E][H][F], the router weight is [E][H]. int8 weights carry one
  *     float32 scale per output row (s_gate, s_up [E][F], s_down [E][H]); the
  *     effective weight is q * s.
+ *   - MOE_I4 (page: 4-bit weights in sections "Inference: the real
+ *     engineering challenge" and "Tradeoffs: when MoE wins and when it
+ *     doesn't", AWQ/GPTQ named, no scheme given): each weight row of K
+ *     values is K/2 bytes, byte j holding k = 2j in its low nibble and
+ *     k = 2j+1 in its high nibble; a nibble is a code u in 0..15 meaning
+ *     u - 8. One float32 scale per row and group of 128 consecutive k:
+ *     s_gate, s_up [E][F][H/128], s_down [E][H][F/128]; the effective weight
+ *     is (u - 8) * s. Supported for T <= 16 (the decode kernels) with H and F
+ *     multiples of 128; otherwise MOE_ERR_UNSUPPORTED.
  *   - Errors: every argument is checked before any HIP call; a failed check
  *     returns a non-zero status and enqueues nothing. A failed kernel launch
  *     returns MOE_ERR_HIP. moe_last_error() gives a message for the last
@@ -70,7 +79,7 @@ typedef enum {
   MOE_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I8 = 2, MOE_I4 = 3 } moe_dtype;
 
 typedef void* moe_stream_t;       /* hipStream_t */
 
@@ -140,13 +149,16 @@ moe_status moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k
  * silu(g) = g / (1 + exp(-g)). Products accumulate in float32; with bf16
  * activations h is rounded to bf16 once (after silu(g)*u) and y_perm once.
  * int8 weights are converted exactly to bf16 and each output column of the
- * float32 accumulator is multiplied by its row scale.
+ * float32 accumulator is multiplied by its row scale; int4 codes are
+ * converted exactly and each 128-k group's partial sum is multiplied by its
+ * scale.
  * Rows at or past offsets[E] of h and y_perm are left unwritten.
  *
  * x [T,H] (act_dtype); perm [T*k] and offsets [E+1] from moe_dispatch;
  * h [T*k,F] and y_perm [T*k,H] (act_dtype, out);
- * s_gate/s_up/s_down must be non-NULL exactly when w_dtype == MOE_I8.
- * Supported (act, weight) pairs: (F32,F32), (BF16,BF16), (BF16,I8).
+ * s_gate/s_up/s_down must be non-NULL exactly when w_dtype is MOE_I8 or
+ * MOE_I4. Supported (act, weight) pairs: (F32,F32), (BF16,BF16), (BF16,I8),
+ * (BF16,I4).
  * ws: device scratch of at least moe_expert_ffn_workspace_bytes(...) bytes
  * (may be 0, then ws may be NULL).
  * ------------------------------------------------------------------------ */
@@ -169,9 +181,10 @@ moe_status moe_expert_ffn(const void* x, moe_dtype act_dtype,
  *
  * moe_expert_gate_up: h[r,:] = silu(x[t] W_gate[e]^T) * (x[t] W_up[e]^T),
  *   t = perm[r] / k, for r in [offsets[e], offsets[e+1]); writes only h.
- *   s_gate / s_up non-NULL exactly when w_dtype == MOE_I8.
+ *   s_gate / s_up non-NULL exactly when w_dtype is MOE_I8 or MOE_I4.
  * moe_expert_down: y_perm[r,:] = h[r,:] W_down[e]^T for the same rows.
- *   s_down non-NULL exactly when w_dtype == MOE_I8; ws as for moe_expert_ffn.
+ *   s_down non-NULL exactly when w_dtype is MOE_I8 or MOE_I4; ws as for
+ *   moe_expert_ffn.
  * Arguments, layouts and rounding are those of moe_expert_ffn.
  * ------------------------------------------------------------------------ */
 moe_status moe_expert_gate_up(const void* x, moe_dtype act_dtype,

@@ -20,7 +20,7 @@ MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE_TOO_SMALL = 3
 MOE_ERR_HIP = 4
 
-MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
 
 # exported symbols and their (restype, argtypes)
 _P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t

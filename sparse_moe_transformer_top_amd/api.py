@@ -12,9 +12,11 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MOE_BF16, MOE_F32, MOE_I8, check
+from ._lib import MOE_BF16, MOE_F32, MOE_I4, MOE_I8, check
 
-_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8}
+# int4 weights travel as packed bytes (two codes per byte) in uint8 tensors
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8, torch.uint8: MOE_I4}
+_WDT = (torch.float32, torch.bfloat16, torch.int8, torch.uint8)
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -83,7 +85,7 @@ def moe_expert_ffn(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, k
     for n, t in (("perm", perm), ("offsets", offsets)):
         _need(t, n, torch.int32, 1)
     for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        _need(t, n, (torch.float32, torch.bfloat16, torch.int8), 3)
+        _need(t, n, _WDT, 3)
     T, H = x.shape
     E, F, _ = w_gate.shape
     h = torch.empty((T * k, F), dtype=x.dtype, device=x.device)
@@ -116,7 +118,10 @@ def moe_expert_down(h: torch.Tensor, offsets: torch.Tensor, T: int, k: int,
                     w_down: torch.Tensor, s_down=None, y_perm: Optional[torch.Tensor] = None):
     """y_perm [T*k,H] = h W_down^T over the dispatched rows."""
     _need(h, "h", (torch.float32, torch.bfloat16), 2)
+    _need(w_down, "w_down", _WDT, 3)
     E, H, F = w_down.shape
+    if w_down.dtype == torch.uint8:
+        F *= 2                       # packed int4: two k per byte
     if y_perm is None:
         y_perm = torch.empty((T * k, H), dtype=h.dtype, device=h.device)
     lib = _lib.load()
@@ -170,7 +175,7 @@ def moe_layer_forward(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Ten
     _need(x, "x", (torch.float32, torch.bfloat16), 2)
     _need(w_router, "w_router", torch.float32, 2)
     for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        _need(t, n, (torch.float32, torch.bfloat16, torch.int8), 3)
+        _need(t, n, _WDT, 3)
     T, H = x.shape
     E, F, _ = w_gate.shape
     dev = x.device

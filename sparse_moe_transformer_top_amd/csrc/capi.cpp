@@ -76,12 +76,25 @@ moe_status check_pair(moe_dtype act, moe_dtype w) {
   moe_status s = check_act(act);
   if (s) return s;
   const bool good = (act == MOE_F32 && w == MOE_F32) ||
-                    (act == MOE_BF16 && (w == MOE_BF16 || w == MOE_I8));
+                    (act == MOE_BF16 && (w == MOE_BF16 || w == MOE_I8 || w == MOE_I4));
   REQUIRE(good, MOE_ERR_UNSUPPORTED,
-          "unsupported (activation, weight) dtypes (%d, %d): use (F32,F32), (BF16,BF16) or "
-          "(BF16,I8)", (int)act, (int)w);
+          "unsupported (activation, weight) dtypes (%d, %d): use (F32,F32), (BF16,BF16), "
+          "(BF16,I8) or (BF16,I4)", (int)act, (int)w);
   return ok();
 }
+
+// int4 weights: decode kernels only (T <= kDecodeMaxT), scale groups of 128 k
+moe_status check_int4(int64_t T, int32_t H, int32_t F, moe_dtype w) {
+  if (w != MOE_I4) return ok();
+  REQUIRE(T <= kDecodeMaxT, MOE_ERR_UNSUPPORTED,
+          "MOE_I4 weights are supported for T <= %lld (decode), got T=%lld",
+          (long long)kDecodeMaxT, (long long)T);
+  REQUIRE(H % 128 == 0 && F % 128 == 0, MOE_ERR_UNSUPPORTED,
+          "MOE_I4 weights need H and F multiples of 128 (got H=%d F=%d)", H, F);
+  return ok();
+}
+
+bool has_scales(moe_dtype w) { return w == MOE_I8 || w == MOE_I4; }
 
 int64_t capacity_of(int64_t T, int32_t k, int32_t E, float cf) {
   if (!(cf > 0.0f) || std::isinf(cf)) return -1;
@@ -157,7 +170,7 @@ moe_status check_ffn_common(int64_t T, int32_t H, int32_t F, int32_t E, int32_t 
                             moe_dtype act, moe_dtype wt) {
   moe_status st;
   if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)) ||
-      (st = check_pair(act, wt)))
+      (st = check_pair(act, wt)) || (st = check_int4(T, H, F, wt)))
     return st;
   return ok();
 }
@@ -240,15 +253,16 @@ moe_status moe_expert_ffn(const void* x, moe_dtype act_dtype, const int32_t* per
                           moe_stream_t stream) {
   moe_status st;
   if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)) ||
-      (st = check_pair(act_dtype, w_dtype)))
+      (st = check_pair(act_dtype, w_dtype)) || (st = check_int4(T, H, F, w_dtype)))
     return st;
   if (T == 0) return ok();  // T-sized buffers may be NULL
   REQUIRE(x && perm && offsets && w_gate && w_up && w_down && h && y_perm,
           MOE_ERR_INVALID_ARGUMENT,
           "x, perm, offsets, w_gate, w_up, w_down, h and y_perm must be non-NULL");
-  const bool i8 = w_dtype == MOE_I8;
+  const bool i8 = has_scales(w_dtype);
   REQUIRE(i8 == (s_gate && s_up && s_down) && (i8 || (!s_gate && !s_up && !s_down)),
-          MOE_ERR_INVALID_ARGUMENT, "scales must be given exactly when weights are MOE_I8");
+          MOE_ERR_INVALID_ARGUMENT,
+          "scales must be given exactly when weights are MOE_I8 or MOE_I4");
   REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) &&
               aligned16(h) && aligned16(y_perm),
           MOE_ERR_INVALID_ARGUMENT, "x, weights, h and y_perm must be 16-byte aligned");
@@ -271,9 +285,9 @@ moe_status moe_expert_gate_up(const void* x, moe_dtype act_dtype, const int32_t*
   if (T == 0) return ok();  // T-sized buffers may be NULL
   REQUIRE(x && perm && offsets && w_gate && w_up && h, MOE_ERR_INVALID_ARGUMENT,
           "x, perm, offsets, w_gate, w_up and h must be non-NULL");
-  const bool i8 = w_dtype == MOE_I8;
+  const bool i8 = has_scales(w_dtype);
   REQUIRE(i8 == (s_gate && s_up) && (i8 || (!s_gate && !s_up)), MOE_ERR_INVALID_ARGUMENT,
-          "scales must be given exactly when weights are MOE_I8");
+          "scales must be given exactly when weights are MOE_I8 or MOE_I4");
   REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(h),
           MOE_ERR_INVALID_ARGUMENT, "x, weights and h must be 16-byte aligned");
   FfnArgs a{x, perm, offsets, T, H, F, E, k, w_gate, w_up, nullptr, s_gate, s_up, nullptr, h,
@@ -291,8 +305,8 @@ moe_status moe_expert_down(const void* h, moe_dtype act_dtype, const int32_t* of
   if (T == 0) return ok();  // T-sized buffers may be NULL
   REQUIRE(h && offsets && w_down && y_perm, MOE_ERR_INVALID_ARGUMENT,
           "h, offsets, w_down and y_perm must be non-NULL");
-  REQUIRE((w_dtype == MOE_I8) == (s_down != nullptr), MOE_ERR_INVALID_ARGUMENT,
-          "s_down must be given exactly when weights are MOE_I8");
+  REQUIRE(has_scales(w_dtype) == (s_down != nullptr), MOE_ERR_INVALID_ARGUMENT,
+          "s_down must be given exactly when weights are MOE_I8 or MOE_I4");
   REQUIRE(aligned16(h) && aligned16(w_down) && aligned16(y_perm), MOE_ERR_INVALID_ARGUMENT,
           "h, w_down and y_perm must be 16-byte aligned");
   const size_t need = ffn_ws_bytes(T, H, F, E, k, act_dtype == MOE_F32 ? ACT_F32 : ACT_BF16,
@@ -358,7 +372,7 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
                              void* ws, size_t ws_bytes, moe_stream_t stream) {
   moe_status st;
   if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)) ||
-      (st = check_pair(act_dtype, w_dtype)))
+      (st = check_pair(act_dtype, w_dtype)) || (st = check_int4(T, H, F, w_dtype)))
     return st;
   REQUIRE(!std::isnan(capacity_factor), MOE_ERR_INVALID_ARGUMENT, "capacity_factor is NaN");
   if (T == 0) {
@@ -370,9 +384,10 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
   }
   REQUIRE(x && w_router && w_gate && w_up && w_down && out, MOE_ERR_INVALID_ARGUMENT,
           "x, w_router, w_gate, w_up, w_down and out must be non-NULL");
-  const bool i8 = w_dtype == MOE_I8;
+  const bool i8 = has_scales(w_dtype);
   REQUIRE(i8 == (s_gate && s_up && s_down) && (i8 || (!s_gate && !s_up && !s_down)),
-          MOE_ERR_INVALID_ARGUMENT, "scales must be given exactly when weights are MOE_I8");
+          MOE_ERR_INVALID_ARGUMENT,
+          "scales must be given exactly when weights are MOE_I8 or MOE_I4");
   REQUIRE(aligned16(x) && aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) &&
               aligned16(w_down) && aligned16(out),
           MOE_ERR_INVALID_ARGUMENT, "x, weights and out must be 16-byte aligned");

@@ -52,6 +52,20 @@ MOE_DEV u32x4 i8x8_to_bf16x8(uint32_t q0, uint32_t q1) {
   return u32x4{a, b, c, d};
 }
 
+// Eight 4-bit codes u (one word; byte j holds element 2j in its low nibble
+// and element 2j+1 in its high nibble) -> eight bf16 values 128 + u, exact:
+// bf16 0x4300 is 128 with an empty 7-bit mantissa, which the code fills. The
+// caller removes the bias. Per output word: one byte permute, one and-or.
+MOE_DEV u32x4 u4x8_to_bf16x8_biased(uint32_t w) {
+  const uint32_t s = w >> 4;   // byte j of s: element 2j+1 in its low nibble
+  u32x4 r;
+  r.x = (__builtin_amdgcn_perm(s, w, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;
+  r.y = (__builtin_amdgcn_perm(s, w, 0x0C050C01u) & 0x000F000Fu) | 0x43004300u;
+  r.z = (__builtin_amdgcn_perm(s, w, 0x0C060C02u) & 0x000F000Fu) | 0x43004300u;
+  r.w = (__builtin_amdgcn_perm(s, w, 0x0C070C03u) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
 MOE_DEV bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 MOE_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

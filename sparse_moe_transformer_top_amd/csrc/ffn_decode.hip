@@ -33,7 +33,23 @@ namespace {
 
 constexpr int kWavesGateUp = 16;
 constexpr int kWavesDown = 8;
+#ifndef MOE_I4_GU_WAVES
+#define MOE_I4_GU_WAVES 8
+#endif
+#ifndef MOE_I4_DN_WAVES
+#define MOE_I4_DN_WAVES 8
+#endif
+// waves per work-group, by weight type
+template <int WT> struct GateUpWaves { static constexpr int N = kWavesGateUp; };
+template <> struct GateUpWaves<WT_I4> { static constexpr int N = MOE_I4_GU_WAVES; };
+template <int WT> struct DownWaves { static constexpr int N = kWavesDown; };
+template <> struct DownWaves<WT_I4> { static constexpr int N = MOE_I4_DN_WAVES; };
+#ifndef MOE_I4_DOWN_SPLIT
+#define MOE_I4_DOWN_SPLIT 8
+#endif
 constexpr int kDownSplit = 8;
+template <int WT> struct DownSplit { static constexpr int N = kDownSplit; };
+template <> struct DownSplit<WT_I4> { static constexpr int N = MOE_I4_DOWN_SPLIT; };
 // k steps each lane keeps in flight, by weight type and number of weight
 // rows per lane (2: gate/up, 1: down). Measured at the Grok-1 decode shape:
 // the bf16 down projection streams about 9% faster with 8 steps than with 4;
@@ -41,13 +57,24 @@ constexpr int kDownSplit = 8;
 // slower with its gate and up rows split over separate waves.
 template <int WT, int NB> struct InFlight { static constexpr int N = 4; };
 template <> struct InFlight<WT_BF16, 1> { static constexpr int N = 8; };
+// int4 needs 64 bytes of activations per 16 bytes of weights per lane
+#ifndef MOE_I4_GU_INF
+#define MOE_I4_GU_INF 2
+#endif
+#ifndef MOE_I4_DN_INF
+#define MOE_I4_DN_INF 4
+#endif
+template <> struct InFlight<WT_I4, 2> { static constexpr int N = MOE_I4_GU_INF; };
+template <> struct InFlight<WT_I4, 1> { static constexpr int N = MOE_I4_DN_INF; };
 
 MOE_DEV u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// A step is 64 bytes of each weight row: 32 k (bf16), 64 k (int8) or 128 k
+// (int4, exactly one scale group); each lane group (lane / 16) reads 16 bytes.
 template <int WT>
 struct Step {
-  static constexpr int K = WT == WT_I8 ? 64 : 32;  // k per MFMA step of one lane group
-  static constexpr int ESZ = WT == WT_I8 ? 1 : 2;  // weight element bytes
+  static constexpr int K = WT == WT_I4 ? 128 : WT == WT_I8 ? 64 : 32;
+  static constexpr int ESZ = WT == WT_I8 ? 1 : 2;  // weight element bytes (bf16, int8)
 };
 
 template <int WT, int NB>
@@ -101,6 +128,59 @@ MOE_DEV void stream_steps(const uint16_t* arow, const char* const (&wrow)[NB], i
   }
 }
 
+// int4 weights: the same round-robin steps (one scale group each). A step's
+// four MFMAs take the codes as bf16 128 + u; four more with a constant -136
+// operand remove the bias (u - 8 is the value), and the step's sum is scaled
+// by the row's group scale into the running sums.
+template <int NB, int W>
+MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB],
+                             const float* const (&srow)[NB], int s_begin, int s_end, int wave,
+                             int g, f32x4 (&acc)[NB]) {
+  constexpr int kInFlight = InFlight<WT_I4, NB>::N;
+  constexpr uint32_t kNeg136 = 0xC308C308u;   // two bf16 -136.0
+  const u32x4 cneg = {kNeg136, kNeg136, kNeg136, kNeg136};
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int s0 = s_begin + wave; s0 < s_end; s0 += W * kInFlight) {
+    u32x4 bv[kInFlight][NB];
+    u32x4 av[kInFlight][4];
+    float sc[kInFlight][NB];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int s = s0 + W * u;
+      if (s < s_end) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          bv[u][b] = ldg16(wrow[b] + (int64_t)s * 64 + 16 * g);
+          sc[u][b] = srow[b][s];
+        }
+        const int k = s * 128 + 32 * g;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) av[u][m] = arow ? ldg16(arow + k + 8 * m) : z;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      if (s0 + W * u < s_end) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const uint32_t wd[4] = {bv[u][b].x, bv[u][b].y, bv[u][b].z, bv[u][b].w};
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(av[u][m]), as_bf16x8(u4x8_to_bf16x8_biased(wd[m])), t, 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][m]), as_bf16x8(cneg), t,
+                                                        0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(sc[u][b], t[v], acc[b][v]);
+        }
+      }
+    }
+  }
+}
+
 // contiguous share [b, e) of n steps for part p of parts
 MOE_DEV void split_range(int n, int parts, int p, int& b, int& e) {
   const int q = (n + parts - 1) / parts;
@@ -110,8 +190,8 @@ MOE_DEV void split_range(int n, int parts, int p, int& b, int& e) {
 
 // Kernel 1: h = silu(x W_gate^T) * (x W_up^T) for <= 16 rows per expert.
 template <int WT>
-__global__ __launch_bounds__(kWavesGateUp * 64) void gateup_decode_kernel(FfnArgs a) {
-  constexpr int kWaves = kWavesGateUp;
+__global__ __launch_bounds__(GateUpWaves<WT>::N * 64) void gateup_decode_kernel(FfnArgs a) {
+  constexpr int kWaves = GateUpWaves<WT>::N;
   __shared__ float red[kWaves][2][4][64];
   const int nt_per_e = (a.F + 15) / 16;
   const int e = blockIdx.x / nt_per_e;
@@ -124,13 +204,21 @@ __global__ __launch_bounds__(kWavesGateUp * 64) void gateup_decode_kernel(FfnArg
   const uint16_t* arow = nullptr;
   if (i < ne) arow = static_cast<const uint16_t*>(a.x) + (int64_t)(a.perm[r0 + i] / a.k) * a.H;
   const int n = min(n0 + i, a.F - 1);
-  const int64_t roff = ((int64_t)e * a.F + n) * a.H * Step<WT>::ESZ;
-  const char* const wrow[2] = {static_cast<const char*>(a.wg) + roff,
-                               static_cast<const char*>(a.wu) + roff};
   f32x4 acc[2];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   acc[1] = acc[0];
-  stream_steps<WT, 2, kWaves>(arow, wrow, 0, a.H / Step<WT>::K, wave, g, acc);
+  if (WT == WT_I4) {
+    const int64_t row = (int64_t)e * a.F + n;
+    const char* const wrow[2] = {static_cast<const char*>(a.wg) + row * (a.H / 2),
+                                 static_cast<const char*>(a.wu) + row * (a.H / 2)};
+    const float* const srow[2] = {a.sg + row * (a.H / 128), a.su + row * (a.H / 128)};
+    stream_steps_i4<2, kWaves>(arow, wrow, srow, 0, a.H / Step<WT>::K, wave, g, acc);
+  } else {
+    const int64_t roff = ((int64_t)e * a.F + n) * a.H * Step<WT>::ESZ;
+    const char* const wrow[2] = {static_cast<const char*>(a.wg) + roff,
+                                 static_cast<const char*>(a.wu) + roff};
+    stream_steps<WT, 2, kWaves>(arow, wrow, 0, a.H / Step<WT>::K, wave, g, acc);
+  }
 
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -163,12 +251,13 @@ __global__ __launch_bounds__(kWavesGateUp * 64) void gateup_decode_kernel(FfnArg
 // Kernel 2: float32 partial sums of y = h W_down^T over one k split, for
 // <= 16 rows per expert: part[split][row][H].
 template <int WT>
-__global__ __launch_bounds__(kWavesDown * 64) void down_decode_kernel(FfnArgs a) {
-  constexpr int kWaves = kWavesDown;
+__global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnArgs a) {
+  constexpr int kWaves = DownWaves<WT>::N;
   __shared__ float red[kWaves][4][64];
   const int nt_per_e = (a.H + 15) / 16;
-  const int split = blockIdx.x % kDownSplit;
-  const int tile = blockIdx.x / kDownSplit;
+  constexpr int kSplit = DownSplit<WT>::N;
+  const int split = blockIdx.x % kSplit;
+  const int tile = blockIdx.x / kSplit;
   const int e = tile / nt_per_e;
   const int n0 = (tile % nt_per_e) * 16;
   const int r0 = a.offsets[e];
@@ -179,13 +268,20 @@ __global__ __launch_bounds__(kWavesDown * 64) void down_decode_kernel(FfnArgs a)
   const uint16_t* arow = i < ne ? static_cast<const uint16_t*>(a.h) + (int64_t)(r0 + i) * a.F
                                 : nullptr;
   const int n = min(n0 + i, a.H - 1);
-  const char* const wrow[1] = {static_cast<const char*>(a.wd) +
-                               ((int64_t)e * a.H + n) * a.F * Step<WT>::ESZ};
   f32x4 acc[1];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   int kb, ke;
-  split_range(a.F / Step<WT>::K, kDownSplit, split, kb, ke);
-  stream_steps<WT, 1, kWaves>(arow, wrow, kb, ke, wave, g, acc);
+  split_range(a.F / Step<WT>::K, kSplit, split, kb, ke);
+  if (WT == WT_I4) {
+    const int64_t row = (int64_t)e * a.H + n;
+    const char* const wrow[1] = {static_cast<const char*>(a.wd) + row * (a.F / 2)};
+    const float* const srow[1] = {a.sd + row * (a.F / 128)};
+    stream_steps_i4<1, kWaves>(arow, wrow, srow, kb, ke, wave, g, acc);
+  } else {
+    const char* const wrow[1] = {static_cast<const char*>(a.wd) +
+                                 ((int64_t)e * a.H + n) * a.F * Step<WT>::ESZ};
+    stream_steps<WT, 1, kWaves>(arow, wrow, kb, ke, wave, g, acc);
+  }
 
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[0][v];
@@ -207,7 +303,7 @@ __global__ __launch_bounds__(kWavesDown * 64) void down_decode_kernel(FfnArgs a)
 }
 
 // y[r, :] = bf16(sum over splits of part[split][r][:]) for r < offsets[E].
-__global__ __launch_bounds__(256) void down_reduce_kernel(FfnArgs a) {
+__global__ __launch_bounds__(256) void down_reduce_kernel(FfnArgs a, int nsplit) {
   const int chunks = a.H / 4;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = gid / chunks;
@@ -217,7 +313,7 @@ __global__ __launch_bounds__(256) void down_reduce_kernel(FfnArgs a) {
   const int64_t stride = a.T * a.k * a.H;
   float4 s = *reinterpret_cast<const float4*>(part + r * a.H + c);
 #pragma unroll
-  for (int p = 1; p < kDownSplit; ++p) {
+  for (int p = 1; p < nsplit; ++p) {
     const float4 v = *reinterpret_cast<const float4*>(part + p * stride + r * a.H + c);
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
@@ -236,23 +332,40 @@ size_t decode_ws_bytes(int64_t T, int H, int k) {
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
   const dim3 grid((unsigned)(a.E * ((a.F + 15) / 16)));
   if (wt == WT_I8)
-    hipLaunchKernelGGL(gateup_decode_kernel<WT_I8>, grid, dim3(kWavesGateUp * 64), 0, s, a);
+    hipLaunchKernelGGL(gateup_decode_kernel<WT_I8>, grid, dim3(GateUpWaves<WT_I8>::N * 64), 0, s,
+                       a);
+  else if (wt == WT_I4)
+    hipLaunchKernelGGL(gateup_decode_kernel<WT_I4>, grid, dim3(GateUpWaves<WT_I4>::N * 64), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL(gateup_decode_kernel<WT_BF16>, grid, dim3(kWavesGateUp * 64), 0, s, a);
+    hipLaunchKernelGGL(gateup_decode_kernel<WT_BF16>, grid, dim3(GateUpWaves<WT_BF16>::N * 64), 0,
+                       s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
-  const dim3 grid((unsigned)(a.E * ((a.H + 15) / 16) * kDownSplit));
-  if (wt == WT_I8)
-    hipLaunchKernelGGL(down_decode_kernel<WT_I8>, grid, dim3(kWavesDown * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL(down_decode_kernel<WT_BF16>, grid, dim3(kWavesDown * 64), 0, s, a);
+  const auto grid = [&](int nsplit) {
+    return dim3((unsigned)(a.E * ((a.H + 15) / 16) * nsplit));
+  };
+  int nsplit = kDownSplit;
+  if (wt == WT_I8) {
+    hipLaunchKernelGGL(down_decode_kernel<WT_I8>, grid(DownSplit<WT_I8>::N),
+                       dim3(DownWaves<WT_I8>::N * 64), 0, s, a);
+    nsplit = DownSplit<WT_I8>::N;
+  } else if (wt == WT_I4) {
+    hipLaunchKernelGGL(down_decode_kernel<WT_I4>, grid(DownSplit<WT_I4>::N),
+                       dim3(DownWaves<WT_I4>::N * 64), 0, s, a);
+    nsplit = DownSplit<WT_I4>::N;
+  } else {
+    hipLaunchKernelGGL(down_decode_kernel<WT_BF16>, grid(DownSplit<WT_BF16>::N),
+                       dim3(DownWaves<WT_BF16>::N * 64), 0, s, a);
+    nsplit = DownSplit<WT_BF16>::N;
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t items = a.T * a.k * (a.H / 4);
   hipLaunchKernelGGL(down_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
-                     a);
+                     a, nsplit);
   return hipGetLastError();
 }
 

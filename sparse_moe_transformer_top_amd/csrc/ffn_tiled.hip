@@ -321,6 +321,7 @@ size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt) {
 }
 
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
+  if (wt == WT_I4) return hipErrorNotSupported;   // int4: decode kernels only
   if (x_needs_wide(a))
     return wt == WT_I8 ? launch_mfma<true, WT_I8, true>(a, s)
                        : launch_mfma<true, WT_BF16, true>(a, s);
@@ -329,6 +330,7 @@ hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
 }
 
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
+  if (wt == WT_I4) return hipErrorNotSupported;
   return wt == WT_I8 ? launch_mfma<false, WT_I8, false>(a, s)
                      : launch_mfma<false, WT_BF16, false>(a, s);
 }

@@ -8,7 +8,7 @@
 namespace moe {
 
 enum Act { ACT_F32 = 0, ACT_BF16 = 1 };
-enum Wt { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2 };
+enum Wt { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2, WT_I4 = 3 };
 
 // router.hip
 hipError_t launch_router_topk(const void* x, Act act, const float* wr, int64_t T, int H,
@@ -35,12 +35,12 @@ struct FfnArgs {
   const int32_t* offsets; // [E+1]
   int64_t T;
   int H, F, E, k;
-  const void* wg;         // [E,F,H]
+  const void* wg;         // [E,F,H] (int4: [E,F,H/2] bytes, two codes per byte)
   const void* wu;         // [E,F,H]
-  const void* wd;         // [E,H,F]
-  const float* sg;        // [E,F] (int8 only)
-  const float* su;        // [E,F]
-  const float* sd;        // [E,H]
+  const void* wd;         // [E,H,F] (int4: [E,H,F/2])
+  const float* sg;        // int8: [E,F] row scales; int4: [E,F,H/128] group scales
+  const float* su;        // as sg
+  const float* sd;        // int8: [E,H]; int4: [E,H,F/128]
   void* h;                // [T*k,F] act
   void* y;                // [T*k,H] act
   void* ws;

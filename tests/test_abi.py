@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 OK, INV, UNS, WS, HIP = 0, 1, 2, 3, 4
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, I4 = 0, 1, 2, 3
 P = 0x10000           # fake, 16-byte aligned device address: never dereferenced
 MIS = 0x10008         # misaligned fake address
 
@@ -97,6 +97,12 @@ def test_expert_ffn_argument_errors(lib):
     assert ffn(lib, F=100) == UNS
     assert ffn(lib, ptrs=dict(wd=MIS)) == INV
     assert ffn(lib, T=0) == OK
+    # int4: decode sizes only, H and F multiples of 128, scales required
+    assert ffn(lib, wdt=I4, T=16) == INV                    # int4 without scales
+    assert ffn(lib, wdt=I4, T=17, scales=(P, P, P)) == UNS
+    assert ffn(lib, wdt=I4, T=8, H=192, scales=(P, P, P)) == UNS
+    assert ffn(lib, wdt=I4, T=8, F=320, scales=(P, P, P)) == UNS
+    assert ffn(lib, act=F32, wdt=I4, T=8, scales=(P, P, P)) == UNS
 
 
 def test_stage_entry_points_argument_errors(lib):

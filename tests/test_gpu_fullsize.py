@@ -46,7 +46,7 @@ def inputs(name):
     return cfg, generate_device(cfg, "cuda")
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "capacity"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "capacity", "decode_i4"])
 def test_fullsize_layer(moe, name):
     cfg, d = inputs(name)
     log(f"full-size {name}: T={cfg.T} {cfg.act}/{cfg.wdt} cf={cfg.capacity_factor}")

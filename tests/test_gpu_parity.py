@@ -3,7 +3,8 @@
 Sizes here run the oracle element by element in seconds and still span
 several GEMM tiles, ragged per-expert tails and column tails; the decode
 kernels (T <= 16) and the tiled kernels (T > 16) are both covered, in bf16,
-int8 and float32, with and without capacity drops.
+int8 and float32, with and without capacity drops, and int4 on the decode
+kernels.
 """
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ from gpu_helpers import (check_close, check_dispatch_equal, check_routing, dev_t
 pytestmark = pytest.mark.gpu
 
 ALL = ["tiny", "p_f32", "p_bf16", "p_bf16_dec", "p_i8", "p_cap", "p_cap_i8", "p_skew",
-       "p_bf16_tail", "p_i8_dec", "p_dec1"]
+       "p_bf16_tail", "p_i8_dec", "p_dec1", "p_i4_dec", "p_i4_dec16", "p_i4_dec1"]
 
 
 @pytest.fixture(scope="module")

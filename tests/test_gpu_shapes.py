@@ -73,7 +73,7 @@ def test_dispatch_on_oracle_indices_general_k(moe):
         check_dispatch_equal({n: host_array(v) for n, v in got.items()}, oracle.dispatch(idx, E, cf))
 
 
-@pytest.mark.parametrize("name", ["p_bf16", "p_i8", "p_bf16_dec", "p_i8_dec"])
+@pytest.mark.parametrize("name", ["p_bf16", "p_i8", "p_bf16_dec", "p_i8_dec", "p_i4_dec"])
 def test_stage_entry_points(moe, name):
     # moe_expert_gate_up then moe_expert_down, each against the oracle
     cfg = synth.get_config(name)
@@ -104,7 +104,7 @@ def test_stage_entry_points(moe, name):
     check_close(yg, y_ref, cfg.act, "down")
 
 
-@pytest.mark.parametrize("name", ["p_bf16", "p_bf16_dec", "p_i8"])
+@pytest.mark.parametrize("name", ["p_bf16", "p_bf16_dec", "p_i8", "p_i4_dec"])
 def test_determinism_each_path(moe, name):
     cfg = synth.get_config(name)
     d = to_device(synth.generate_host(cfg))
