@@ -48,6 +48,7 @@ def source_sha(files):
 
 KERNEL_SOURCES = {
     "gateup_decode": ["sparse_moe_transformer_top_amd/csrc/ffn_decode.hip",
+                      "sparse_moe_transformer_top_amd/csrc/ffn_decode_lds.hip",
                       "sparse_moe_transformer_top_amd/csrc/common.h"],
     "gateup_tiled": ["sparse_moe_transformer_top_amd/csrc/ffn_tiled.hip",
                      "sparse_moe_transformer_top_amd/csrc/common.h",
@@ -266,8 +267,10 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles("gateup_decode", cfg.name),
-                "kernel": "gateup_decode_kernel (%s weights)" % {
-                    "bf16": "bf16", "i8": "int8", "i4": "int4"}[cfg.wdt],
+                "kernel": ("gateup_xlds_kernel (bf16 weights, token rows in LDS)"
+                           if cfg.wdt == "bf16" and cfg.T <= 8 else
+                           "gateup_decode_kernel (%s weights)" % {
+                               "bf16": "bf16", "i8": "int8", "i4": "int4"}[cfg.wdt]),
                 "algorithmic_bytes": int(gu_bytes), "mean_ms": round(gu_ms, 4)}
     else:
         achieved = gu_flops / (gu_ms * 1e-3) / 1e12

@@ -330,6 +330,9 @@ size_t decode_ws_bytes(int64_t T, int H, int k) {
 }
 
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
+  // up to 8 tokens with bf16 weights: the LDS-staged kernel (ffn_decode_lds.hip)
+  const hipError_t e = launch_gateup_decode_lds(a, wt, s);
+  if (e != hipErrorNotSupported) return e;
   const dim3 grid((unsigned)(a.E * ((a.F + 15) / 16)));
   if (wt == WT_I8)
     hipLaunchKernelGGL(gateup_decode_kernel<WT_I8>, grid, dim3(GateUpWaves<WT_I8>::N * 64), 0, s,

@@ -48,6 +48,13 @@ struct FfnArgs {
 
 // largest T for which the decode (few rows per expert) kernels are used
 constexpr int64_t kDecodeMaxT = 16;
+// gate/up with the expert's token rows in LDS (ffn_decode_lds.hip, bf16
+// weights): up to this many tokens, when their rows fit one work-group's LDS
+constexpr int64_t kDecodeLdsMaxT = 8;
+constexpr size_t kDecodeLdsMax = 160 * 1024;
+size_t decode_lds_bytes(int64_t T, int H);
+// hipErrorNotSupported (nothing launched) when T or the LDS need is too large
+hipError_t launch_gateup_decode_lds(const FfnArgs& a, Wt wt, hipStream_t s);
 
 size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt);
 // gate/up product with the SwiGLU epilogue (writes h) and down product (writes y)

@@ -43,6 +43,13 @@ SHAPES = [
     ("t17_tiled", 17, 512, 640, 8, 2, "bf16", "bf16", None),
     ("t16_dec_i8", 16, 512, 640, 8, 2, "bf16", "i8", None),
     ("e2_k2", 90, 256, 256, 2, 2, "bf16", "bf16", 0.75),
+    # T <= 8, bf16: the gate/up kernel with the token rows in LDS; ragged F
+    # (idle waves in the last work-group), H not a multiple of 128, E = 16
+    ("t8_lds_tail", 8, 320, 448, 8, 2, "bf16", "bf16", None),
+    ("t3_lds_e16k4", 3, 256, 384, 16, 4, "bf16", "bf16", None),
+    # rows too wide for LDS: falls back to the split-k decode kernel
+    ("t8_wide_h", 8, 10240, 128, 8, 2, "bf16", "bf16", None),
+    ("t8_i8_i4", 8, 384, 256, 8, 2, "bf16", "i4", None),
 ]
 
 
