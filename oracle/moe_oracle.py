@@ -358,3 +358,58 @@ def routing_stats(l32: np.ndarray, k: int, counts: np.ndarray) -> RoutingStats:
     util = counts * E / (T * k) if T else np.zeros(E)
     return RoutingStats(margin, mass, util)
 
+
+# --------------------------------------------------------------------------
+# expert parallelism: the data movement around the all-to-all (the page,
+# section "Expert parallelism vs. tensor parallelism": EP places whole
+# experts on ranks; each rank routes its own tokens, sends them to the ranks
+# of their experts, runs its local experts and gathers the outputs back).
+# Experts are placed in contiguous blocks: rank r holds E/R experts
+# r*E/R ... (r+1)*E/R - 1. The exchange itself is not modelled here; these
+# are the layouts on either side of it.
+# --------------------------------------------------------------------------
+
+
+def ep_pack(x: np.ndarray, perm: np.ndarray, offsets: np.ndarray, k: int, E: int, R: int):
+    """Rows a rank sends: the x row of every kept assignment, in dispatch
+    order (grouped by expert, hence by destination rank), and the number of
+    rows for each destination rank."""
+    if E % R:
+        raise ValueError("E must be a multiple of R")
+    n = int(offsets[E])
+    rows = np.asarray(x)[np.asarray(perm[:n], np.int64) // k]
+    per = E // R
+    counts = np.array([offsets[(r + 1) * per] - offsets[r * per] for r in range(R)], np.int64)
+    return rows, counts
+
+
+def ep_recv_layout(recv_counts: np.ndarray):
+    """recv_counts[p][e]: rows received from source rank p for local expert e
+    (the receive buffer holds source 0's rows, then source 1's, ..., each
+    source's rows grouped by local expert). Returns (offsets [E_local+1] of
+    the rows regrouped by local expert, then source; row_index: for each
+    regrouped row, its position in the receive buffer)."""
+    c = np.asarray(recv_counts, np.int64)
+    R, El = c.shape
+    start = np.zeros((R, El), np.int64)
+    pos = 0
+    for p in range(R):
+        for e in range(El):
+            start[p, e] = pos
+            pos += c[p, e]
+    row_index, offsets = [], [0]
+    for e in range(El):
+        for p in range(R):
+            row_index.extend(range(start[p, e], start[p, e] + c[p, e]))
+        offsets.append(len(row_index))
+    return np.array(offsets, np.int64), np.array(row_index, np.int64)
+
+
+def ep_unpack(y_rows: np.ndarray, row_index: np.ndarray, n_recv: int) -> np.ndarray:
+    """Expert outputs (regrouped order) back to receive-buffer order, ready
+    for the return exchange: back[row_index[j]] = y_rows[j]."""
+    y_rows = np.asarray(y_rows)
+    back = np.zeros((n_recv,) + y_rows.shape[1:], y_rows.dtype)
+    back[np.asarray(row_index, np.int64)] = y_rows
+    return back
+
