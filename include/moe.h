@@ -238,6 +238,43 @@ moe_status moe_routing_stats(const float* logits, const int32_t* counts, int64_t
                              float* unselected_mass, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Expert parallelism: the layouts on either side of the all-to-all (the
+ * exchange itself is the caller's, e.g. RCCL). Page: section "Expert
+ * parallelism vs. tensor parallelism" (EP forward: route locally, send each
+ * token to its experts' ranks, run the local experts, gather the outputs
+ * back). Experts sit in contiguous blocks of E/R on R ranks (E % R == 0,
+ * 1 <= R <= 64), so rows in dispatch order are grouped by destination rank.
+ *
+ * moe_ep_pack: send_buf[j,:] = x[perm[j] / k, :] for j < offsets[E] (the kept
+ *   rows, dispatch order); send_counts[r] = rows for rank r. x [T,H] and
+ *   send_buf [T*k,H] in act_dtype (16-byte aligned); perm, offsets from
+ *   moe_dispatch; send_counts [R] int32.
+ * moe_ep_recv_layout: recv_counts [R][E_local] int32 (rows received from
+ *   source p for local expert e; the receive buffer holds source 0's rows,
+ *   then source 1's, each grouped by local expert). Writes local_offsets
+ *   [E_local+1] of the rows regrouped by local expert, then source, and
+ *   row_index [max_rows]: the receive-buffer row of each regrouped row. The
+ *   local experts then run as moe_expert_ffn(x = receive buffer, perm =
+ *   row_index, offsets = local_offsets, k = 1, T = receive rows). Rows whose
+ *   regrouped position would reach max_rows are not written and the offsets
+ *   are capped at max_rows.
+ * moe_ep_unpack: back_buf[row_index[j],:] = y_rows[j,:] for
+ *   j < local_offsets[E_local]: expert outputs in receive order for the
+ *   return exchange (y_rows [max_rows,H], back_buf with as many rows as the
+ *   receive buffer, act_dtype, 16-byte aligned). After the exchange each
+ *   source holds its rows in its own dispatch order: moe_combine's y_perm.
+ * ------------------------------------------------------------------------ */
+moe_status moe_ep_pack(const void* x, moe_dtype act_dtype, const int32_t* perm,
+                       const int32_t* offsets, int64_t T, int32_t H, int32_t E, int32_t k,
+                       int32_t R, void* send_buf, int32_t* send_counts, moe_stream_t stream);
+moe_status moe_ep_recv_layout(const int32_t* recv_counts, int32_t R, int32_t E_local,
+                              int64_t max_rows, int32_t* local_offsets, int32_t* row_index,
+                              moe_stream_t stream);
+moe_status moe_ep_unpack(const void* y_rows, moe_dtype act_dtype, const int32_t* row_index,
+                         const int32_t* local_offsets, int32_t E_local, int32_t H,
+                         int64_t max_rows, void* back_buf, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * The whole layer: router_topk -> dispatch -> expert_ffn -> combine on one
  * stream, with no host synchronisation. Page: GrokMoELayer.forward.
  *

@@ -9,6 +9,9 @@ from .api import (  # noqa: F401
     layer_workspace_bytes,
     moe_combine,
     moe_dispatch,
+    moe_ep_pack,
+    moe_ep_recv_layout,
+    moe_ep_unpack,
     moe_expert_down,
     moe_expert_ffn,
     moe_expert_gate_up,

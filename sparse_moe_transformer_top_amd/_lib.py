@@ -39,6 +39,9 @@ SIGNATURES = {
                                   _P, _P, _P, _SZ, _P]),
     "moe_combine": (C.c_int, [_P, _P, _P, _I64, _I32, _I32, C.c_int, _P, _P]),
     "moe_routing_stats": (C.c_int, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P]),
+    "moe_ep_pack": (C.c_int, [_P, C.c_int, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_ep_recv_layout": (C.c_int, [_P, _I32, _I32, _I64, _P, _P, _P]),
+    "moe_ep_unpack": (C.c_int, [_P, C.c_int, _P, _P, _I32, _I32, _I64, _P, _P]),
     "moe_layer_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, C.c_int, C.c_int]),
     "moe_layer_forward": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _P, _P, _P, _I64, _I32,
                                     _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -161,6 +161,44 @@ def moe_routing_stats(logits: torch.Tensor, counts: torch.Tensor, k: int):
     return out
 
 
+def moe_ep_pack(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, k: int, R: int):
+    """(send_buf [T*k,H] in x's dtype: the kept rows in dispatch order, rows past
+    offsets[E] unwritten; send_counts [R] int32: rows for each rank)."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    T, H = x.shape
+    E = offsets.numel() - 1
+    send = torch.empty((T * k, H), dtype=x.dtype, device=x.device)
+    counts = torch.empty(R, dtype=torch.int32, device=x.device)
+    check(_lib.load().moe_ep_pack(_p(x), _DT[x.dtype], _p(perm), _p(offsets), T, H, E, k, R,
+                                  _p(send), _p(counts), _stream(x.device)))
+    return send, counts
+
+
+def moe_ep_recv_layout(recv_counts: torch.Tensor, max_rows: int):
+    """(local_offsets [E_local+1], row_index [max_rows]) int32 from
+    recv_counts [R, E_local] int32."""
+    _need(recv_counts, "recv_counts", torch.int32, 2)
+    R, El = recv_counts.shape
+    dev = recv_counts.device
+    off = torch.empty(El + 1, dtype=torch.int32, device=dev)
+    idx = torch.empty(max(max_rows, 1), dtype=torch.int32, device=dev)
+    check(_lib.load().moe_ep_recv_layout(_p(recv_counts), R, El, max_rows, _p(off), _p(idx),
+                                         _stream(dev)))
+    return off, idx[:max_rows]
+
+
+def moe_ep_unpack(y_rows: torch.Tensor, row_index: torch.Tensor, local_offsets: torch.Tensor,
+                  n_recv: int):
+    """back [n_recv, H]: back[row_index[j]] = y_rows[j] for j < local_offsets[-1]."""
+    _need(y_rows, "y_rows", (torch.float32, torch.bfloat16), 2)
+    max_rows, H = y_rows.shape
+    back = torch.empty((n_recv, H), dtype=y_rows.dtype, device=y_rows.device)
+    check(_lib.load().moe_ep_unpack(_p(y_rows), _DT[y_rows.dtype], _p(row_index),
+                                    _p(local_offsets), local_offsets.numel() - 1, H, max_rows,
+                                    _p(back), _stream(y_rows.device)))
+    return back
+
+
 def layer_workspace_bytes(T: int, H: int, F: int, E: int, k: int, act: torch.dtype,
                           wdt: torch.dtype) -> int:
     return _lib.load().moe_layer_workspace_bytes(T, H, F, E, k, _DT[act], _DT[wdt])

@@ -357,6 +357,63 @@ moe_status moe_routing_stats(const float* logits, const int32_t* counts, int64_t
                     "routing statistics launch");
 }
 
+moe_status moe_ep_pack(const void* x, moe_dtype act_dtype, const int32_t* perm,
+                       const int32_t* offsets, int64_t T, int32_t H, int32_t E, int32_t k,
+                       int32_t R, void* send_buf, int32_t* send_counts, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_act(act_dtype)))
+    return st;
+  REQUIRE(R >= 1 && R <= 64, MOE_ERR_UNSUPPORTED, "R=%d ranks: 1 <= R <= 64 supported", R);
+  REQUIRE(E % R == 0, MOE_ERR_INVALID_ARGUMENT, "E=%d is not a multiple of R=%d", E, R);
+  REQUIRE(offsets && send_counts, MOE_ERR_INVALID_ARGUMENT,
+          "offsets and send_counts must be non-NULL");
+  if (T > 0) {
+    REQUIRE(x && perm && send_buf, MOE_ERR_INVALID_ARGUMENT,
+            "x, perm and send_buf must be non-NULL");
+    REQUIRE(aligned16(x) && aligned16(send_buf), MOE_ERR_INVALID_ARGUMENT,
+            "x and send_buf must be 16-byte aligned");
+  }
+  return hip_status(launch_ep_pack(x, (int64_t)H * act_size(act_dtype), perm, offsets, T * k, E,
+                                   k, R, send_buf, send_counts, (hipStream_t)stream),
+                    "EP pack launch");
+}
+
+moe_status moe_ep_recv_layout(const int32_t* recv_counts, int32_t R, int32_t E_local,
+                              int64_t max_rows, int32_t* local_offsets, int32_t* row_index,
+                              moe_stream_t stream) {
+  REQUIRE(R >= 1 && R <= 64, MOE_ERR_UNSUPPORTED, "R=%d ranks: 1 <= R <= 64 supported", R);
+  REQUIRE(E_local >= 1 && E_local <= 16, MOE_ERR_UNSUPPORTED,
+          "E_local=%d: 1 <= E_local <= 16 supported", E_local);
+  REQUIRE(max_rows >= 0 && max_rows < ((int64_t)1 << 31), MOE_ERR_INVALID_ARGUMENT,
+          "max_rows=%lld must be in [0, 2^31)", (long long)max_rows);
+  REQUIRE(recv_counts && local_offsets && (row_index || max_rows == 0),
+          MOE_ERR_INVALID_ARGUMENT,
+          "recv_counts, local_offsets and row_index (unless max_rows == 0) must be non-NULL");
+  return hip_status(launch_ep_recv_layout(recv_counts, R, E_local, max_rows, local_offsets,
+                                          row_index, (hipStream_t)stream),
+                    "EP receive layout launch");
+}
+
+moe_status moe_ep_unpack(const void* y_rows, moe_dtype act_dtype, const int32_t* row_index,
+                         const int32_t* local_offsets, int32_t E_local, int32_t H,
+                         int64_t max_rows, void* back_buf, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_dim("H", H)) || (st = check_act(act_dtype))) return st;
+  REQUIRE(E_local >= 1 && E_local <= 16, MOE_ERR_UNSUPPORTED,
+          "E_local=%d: 1 <= E_local <= 16 supported", E_local);
+  REQUIRE(max_rows >= 0 && max_rows < ((int64_t)1 << 31), MOE_ERR_INVALID_ARGUMENT,
+          "max_rows=%lld must be in [0, 2^31)", (long long)max_rows);
+  if (max_rows == 0) return ok();
+  REQUIRE(y_rows && row_index && local_offsets && back_buf, MOE_ERR_INVALID_ARGUMENT,
+          "y_rows, row_index, local_offsets and back_buf must be non-NULL");
+  REQUIRE(aligned16(y_rows) && aligned16(back_buf), MOE_ERR_INVALID_ARGUMENT,
+          "y_rows and back_buf must be 16-byte aligned");
+  return hip_status(launch_ep_unpack(y_rows, (int64_t)H * act_size(act_dtype), row_index,
+                                     local_offsets, E_local, max_rows, back_buf,
+                                     (hipStream_t)stream),
+                    "EP unpack launch");
+}
+
 size_t moe_layer_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                                  moe_dtype act_dtype, moe_dtype w_dtype) {
   if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1) return 0;

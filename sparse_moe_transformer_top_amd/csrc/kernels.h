@@ -70,4 +70,14 @@ hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_routing_stats(const float* logits, const int32_t* counts, int64_t T, int E,
                                 int k, float* util, float* margin, float* mass, hipStream_t s);
 
+// expert-parallel layouts (ep.hip)
+hipError_t launch_ep_pack(const void* x, int64_t row_bytes, const int32_t* perm,
+                          const int32_t* offsets, int64_t max_rows, int E, int k, int R,
+                          void* send, int32_t* send_counts, hipStream_t s);
+hipError_t launch_ep_recv_layout(const int32_t* counts, int R, int El, int64_t max_rows,
+                                 int32_t* offsets, int32_t* row_index, hipStream_t s);
+hipError_t launch_ep_unpack(const void* y, int64_t row_bytes, const int32_t* row_index,
+                            const int32_t* offsets, int El, int64_t max_rows, void* back,
+                            hipStream_t s);
+
 }  // namespace moe

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -133,6 +133,31 @@ def test_routing_stats_argument_errors(lib):
     assert st(P, P, 8, 17, 2, None, P, None, None) == UNS
     assert st(P, P, 8, 8, 5, None, P, None, None) == UNS
     assert st(P, P, -1, 8, 2, None, P, None, None) == INV
+
+
+def test_ep_argument_errors(lib):
+    pk = lambda **kw: lib.moe_ep_pack(kw.get("x", P), BF16, P, P, kw.get("T", 8), 128,
+                                      kw.get("E", 8), 2, kw.get("R", 2), kw.get("send", P),
+                                      kw.get("cnt", P), None)
+    assert pk(R=3) == INV                 # E not a multiple of R
+    assert pk(R=65, E=8) == UNS
+    assert pk(cnt=None) == INV
+    assert pk(send=None) == INV
+    assert pk(x=MIS) == INV
+    rl = lambda **kw: lib.moe_ep_recv_layout(P, kw.get("R", 2), kw.get("El", 4),
+                                             kw.get("mr", 100), kw.get("off", P),
+                                             kw.get("idx", P), None)
+    assert rl(R=0) == UNS
+    assert rl(El=17) == UNS
+    assert rl(mr=-1) == INV
+    assert rl(idx=None) == INV
+    assert rl(off=None) == INV
+    up = lambda **kw: lib.moe_ep_unpack(kw.get("y", P), BF16, P, P, kw.get("El", 4), 128,
+                                        kw.get("mr", 100), kw.get("back", P), None)
+    assert up(mr=0) == OK
+    assert up(back=None) == INV
+    assert up(y=MIS) == INV
+    assert up(El=0) == UNS
 
 
 def test_combine_argument_errors(lib):

@@ -1,0 +1,129 @@
+"""GPU parity of the expert-parallel layouts (moe_ep_pack, moe_ep_recv_layout,
+moe_ep_unpack) and of the whole EP data path on R emulated ranks of one GPU.
+
+The all-to-all is emulated by slicing device tensors on the host side of the
+test (rank r receives, from every source, the rows of its experts); every
+layout step and the experts run through the C ABI. Layouts are compared
+bit-exactly with the oracle's on the oracle's own dispatch; the EP output of
+every rank must equal the single-device layer (bitwise when both run the same
+GEMM kernel, else within the bf16 tolerance) and the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import check_close, dev_tensor, host_array, log, out_as_f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import sparse_moe_transformer_top_amd as m
+    m.load_library()
+    return m
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 8])
+def test_pack_and_layout_match_oracle(moe, R):
+    cfg = synth.get_config("p_bf16")
+    inp = synth.generate_host(cfg)
+    d = to_device(inp)
+    E, k, El = cfg.E, cfg.k, cfg.E // R
+    l32, l64 = oracle.router_logits(oracle.widen(inp.x, cfg.act), inp.wr)
+    disp = oracle.dispatch(oracle.top_k_softmax(l32, l64, k).idx, E, 1.0)   # with drops
+    send, cnt = moe.moe_ep_pack(d["x"], dev_tensor(disp.perm, "i32"),
+                                dev_tensor(disp.offsets, "i32"), k, R)
+    torch.cuda.synchronize()
+    rows, rcnt = oracle.ep_pack(inp.x, disp.perm, disp.offsets, k, E, R)
+    n = int(disp.offsets[E])
+    assert np.array_equal(host_array(cnt), rcnt)
+    assert np.array_equal(host_array(send)[:n], rows)          # bf16 bits, bit-exact
+    # a receive layout from seeded counts, and the unpack that inverts it
+    rc = np.random.default_rng(R).integers(0, 40, (R, El)).astype(np.int32)
+    rc[0, 0] = 0                                               # an empty segment
+    n_recv = int(rc.sum())
+    off, idx = moe.moe_ep_recv_layout(dev_tensor(rc, "i32"), n_recv)
+    torch.cuda.synchronize()
+    roff, ridx = oracle.ep_recv_layout(rc)
+    assert np.array_equal(host_array(off), roff)
+    assert np.array_equal(host_array(idx), ridx)
+    y = torch.randn(n_recv, cfg.H, device="cuda").to(torch.bfloat16)
+    back = moe.moe_ep_unpack(y, idx, off, n_recv)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_array(back), oracle.ep_unpack(host_array(y), ridx, n_recv))
+
+
+def test_recv_layout_caps_at_max_rows(moe):
+    rc = np.array([[5, 7], [3, 9]], np.int32)                  # 24 rows
+    off, idx = moe.moe_ep_recv_layout(dev_tensor(rc, "i32"), 10)
+    torch.cuda.synchronize()
+    roff, ridx = oracle.ep_recv_layout(rc)
+    assert host_array(off).tolist() == np.minimum(roff, 10).tolist()
+    assert np.array_equal(host_array(idx), ridx[:10])
+
+
+@pytest.mark.parametrize("R,name", [(2, "p_bf16"), (4, "p_bf16"), (8, "p_bf16"),
+                                    (4, "p_i8"), (2, "p_dec1")])
+def test_ep_path_equals_layer(moe, R, name):
+    cfg = synth.get_config(name)
+    if cfg.T < 2 * R:
+        cfg = cfg.with_(T=2 * R + 3)
+    inp = synth.generate_host(cfg)
+    d = to_device(inp)
+    E, k, El = cfg.E, cfg.k, cfg.E // R
+    log(f"EP path {name} on {R} emulated ranks")
+    cuts = np.linspace(0, cfg.T, R + 1).astype(int)
+    src = []
+    for p in range(R):
+        x = d["x"][cuts[p]:cuts[p + 1]].contiguous()
+        idx, w = moe.moe_router_topk(x, d["wr"], k)
+        disp = moe.moe_dispatch(idx, E, None)
+        send, cnt = moe.moe_ep_pack(x, disp["perm"], disp["offsets"], k, R)
+        src.append(dict(x=x, w=w, disp=disp, send=send, cnt=host_array(cnt),
+                        ecnt=np.diff(host_array(disp["offsets"]))))
+    torch.cuda.synchronize()
+    returned = {p: [] for p in range(R)}
+    all_tiled = True     # every destination's expert GEMMs took the tiled (T > 16) kernels
+    sl = lambda t, e0, e1: None if t is None else t[e0:e1].contiguous()
+    for r in range(R):
+        parts, rc = [], np.zeros((R, El), np.int32)
+        for p, s in enumerate(src):
+            s0 = int(s["cnt"][:r].sum())
+            parts.append(s["send"][s0:s0 + int(s["cnt"][r])])
+            rc[p] = s["ecnt"][r * El:(r + 1) * El]
+        recv = torch.cat(parts).contiguous()
+        n_recv = recv.shape[0]
+        all_tiled &= n_recv == 0 or n_recv > 16
+        off, ridx = moe.moe_ep_recv_layout(dev_tensor(rc, "i32"), n_recv)
+        if n_recv:
+            e0, e1 = r * El, (r + 1) * El
+            _, y = moe.moe_expert_ffn(recv, ridx, off, 1, sl(d["wg"], e0, e1),
+                                      sl(d["wu"], e0, e1), sl(d["wd"], e0, e1),
+                                      sl(d["sg"], e0, e1), sl(d["su"], e0, e1),
+                                      sl(d["sd"], e0, e1))
+            back = moe.moe_ep_unpack(y, ridx, off, n_recv)
+        else:
+            back = recv
+        pos = 0
+        for p in range(R):
+            n = int(rc[p].sum())
+            returned[p].append(back[pos:pos + n])
+            pos += n
+    for p, s in enumerate(src):
+        y_perm = torch.cat(returned[p]).contiguous()
+        out = moe.moe_combine(y_perm, s["disp"]["slot_row"], s["w"])
+        ref = moe.moe_layer_forward(s["x"], d["wr"], d["wg"], d["wu"], d["wd"], k=k,
+                                    s_gate=d["sg"], s_up=d["su"], s_down=d["sd"])
+        torch.cuda.synchronize()
+        xs = inp.x[cuts[p]:cuts[p + 1]]
+        res = oracle.layer_forward(xs, cfg.act, inp.wr, inp.wg, inp.wu, inp.wd, cfg.wdt, k=k,
+                                   sg=inp.sg, su=inp.su, sd=inp.sd)
+        check_close(out_as_f64(out), res.out, cfg.act, f"EP rank {p}")
+        if all_tiled and xs.shape[0] > 16:
+            # tiled GEMMs on both sides: per element, the same products in the same order
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        else:
+            check_close(out_as_f64(out), out_as_f64(ref), cfg.act, f"EP rank {p} vs layer")
