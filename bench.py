@@ -161,6 +161,36 @@ class Layer:
         return a.elapsed_time(b) / reps
 
 
+    def ep_layout_time(self, R, reps=20):
+        """Mean durations (ms) of moe_ep_pack and moe_ep_unpack for this
+        workload's dispatch with the E experts on R ranks, the rows of all
+        ranks' receive buffers handled on this GPU (pack: every kept row read
+        and written once; unpack the same), queued behind a device-side delay."""
+        torch, d, c, m = self.torch, self.d, self.cfg, self.moe
+        idx, _ = m.moe_router_topk(d.x, d.wr, c.k)
+        disp = m.moe_dispatch(idx, c.E, c.capacity_factor)
+        send, cnt = m.moe_ep_pack(d.x, disp["perm"], disp["offsets"], c.k, R)
+        n = int(disp["offsets"][-1].item())
+        # one receive buffer holding everything: R x E/R counts from this dispatch
+        rc = torch.diff(disp["offsets"]).view(1, c.E).to(torch.int32).contiguous()
+        off, ridx = m.moe_ep_recv_layout(rc, n)
+        y = send[:n]
+        out = []
+        for fn in (lambda: m.moe_ep_pack(d.x, disp["perm"], disp["offsets"], c.k, R),
+                   lambda: m.moe_ep_unpack(y, ridx, off, n)):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(2_000_000)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / reps)
+        return out[0], out[1], n
+
+
 def cpu_baseline(layer, n_tokens):
     """The oracle on the first n_tokens tokens of the workload (routing and
     dispatch over all T tokens, expert FFN and combine for the sample)."""
@@ -307,6 +337,16 @@ def main():
     result["routing_stats"] = {"us": round(rs_ms * 1e3, 2), "bytes": rs_bytes,
                                "GBps": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1)}
 
+    # expert-parallel layouts (E experts on E ranks): pack and unpack each read
+    # and write every kept row once
+    pk_ms, up_ms, n_rows = layer.ep_layout_time(cfg.E)
+    ep_bytes = 2 * n_rows * H * asz
+    result["ep_layout"] = {"ranks": cfg.E, "rows": n_rows,
+                           "pack_us": round(pk_ms * 1e3, 2),
+                           "pack_GBps": round(ep_bytes / (pk_ms * 1e-3) / 1e9, 1),
+                           "unpack_us": round(up_ms * 1e3, 2),
+                           "unpack_GBps": round(ep_bytes / (up_ms * 1e-3) / 1e9, 1)}
+
     if not args.no_prefill and cfg.name == "decode":
         pcfg = synth.CONFIGS["prefill"]
         log("prefill secondary line: same weights, T=8192 tokens")
@@ -323,6 +363,12 @@ def main():
                         "TFLOPs": round(4.0 * H * F * pk / (pgu * 1e-3) / 1e12, 1)},
             "down": {"ms": round(pdn, 3),
                      "TFLOPs": round(2.0 * H * F * pk / (pdn * 1e-3) / 1e12, 1)}}
+        ppk, pup, prows = pl.ep_layout_time(pcfg.E)
+        pbytes = 2 * prows * H * 2
+        result["prefill"]["ep_layout"] = {
+            "ranks": pcfg.E, "rows": prows, "pack_us": round(ppk * 1e3, 1),
+            "pack_GBps": round(pbytes / (ppk * 1e-3) / 1e9, 1), "unpack_us": round(pup * 1e3, 1),
+            "unpack_GBps": round(pbytes / (pup * 1e-3) / 1e9, 1)}
         del pl
         torch.cuda.empty_cache()
 
