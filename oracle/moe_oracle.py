@@ -297,6 +297,107 @@ def layer_forward(x: np.ndarray, act: str, wr: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# the layer's backward (training). The page gives the forward only and marks
+# the capacity drop as a training-time step; the backward here is the chain
+# rule applied to that forward, taken exactly: the top-k choice and the
+# capacity drop are piecewise constant in the inputs, so no gradient flows
+# through the selection; a dropped slot contributes nothing to the output
+# and so receives no gradient; the routing weights are a softmax over the k
+# selected logits, whose Jacobian couples the selected slots of a token.
+# --------------------------------------------------------------------------
+
+
+def silu_grad(g: np.ndarray) -> np.ndarray:
+    """d silu / dg = s + g s (1 - s), s = 1 / (1 + exp(-g))."""
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-g))
+    return s + g * s * (1.0 - s)
+
+
+@dataclass
+class LayerGrads:
+    routing: Routing
+    disp: Dispatch
+    out: np.ndarray      # [T,H] forward output
+    dx: np.ndarray       # [T,H]
+    dwr: np.ndarray      # [E,H]
+    dwg: np.ndarray      # [E,F,H]
+    dwu: np.ndarray      # [E,F,H]
+    dwd: np.ndarray      # [E,H,F]
+    dw: np.ndarray       # [T,k] gradient of the routing weights (0 for dropped slots)
+    dlogits: np.ndarray  # [T,E] gradient of the router logits
+
+
+def layer_backward(x: np.ndarray, act: str, wr: np.ndarray,
+                   wg: Sequence, wu: Sequence, wd: Sequence, wdt: str,
+                   dout: np.ndarray, k: int = 2, capacity_factor=None,
+                   tie_tol: float = 1e-4) -> LayerGrads:
+    """Gradients of L = sum(dout * out) for the layer of layer_forward, in
+    float64 on the stored values (routing decided as in layer_forward).
+
+    For a kept slot (t, j) routed to expert e, with row x_t:
+      g = x_t Wg_e^T, u = x_t Wu_e^T, h = silu(g) * u, y = h Wd_e^T
+      dw[t,j]  = dout_t . y                     (out_t = sum_j w[t,j] y_(t,j))
+      dy       = w[t,j] * dout_t
+      dh       = dy Wd_e
+      dg       = dh * u * silu'(g),  du = dh * silu(g)
+      dWd_e   += dy^T h,  dWg_e += dg^T x_t,  dWu_e += du^T x_t
+      dx_t    += dg Wg_e + du Wu_e
+    Softmax over the selected logits, w_j = exp(l_j) / sum_j' exp(l_j'):
+      dl[t, idx[t,j]] = w_j (dw_j - sum_j' w_j' dw_j'), zero for unselected
+    Router, logits = x Wr^T:  dx_t += dl_t Wr,  dWr = dl^T x."""
+    x64 = widen(x, act)
+    T, H = x64.shape
+    wr64 = np.asarray(wr, np.float32).astype(np.float64)
+    E = wr64.shape[0]
+    d64 = np.asarray(dout, np.float64)
+    l32, l64 = router_logits(x64, wr)
+    routing = top_k_softmax(l32, l64, k, tie_tol)
+    disp = dispatch(routing.idx, E, capacity_factor)
+
+    F = widen(wg[0], wdt).shape[0]
+    out = np.zeros((T, H))
+    dx = np.zeros((T, H))
+    dwg = np.zeros((E, F, H))
+    dwu = np.zeros((E, F, H))
+    dwd = np.zeros((E, H, F))
+    dw = np.zeros((T, k))
+    for e in range(E):
+        # the expert's kept slots in dispatch order
+        rows = range(int(disp.offsets[e]), int(disp.offsets[e + 1]))
+        slots = [int(disp.perm[r]) for r in rows]
+        if not slots:
+            continue
+        ts = np.array([a // k for a in slots])
+        js = np.array([a % k for a in slots])
+        Wg, Wu, Wd = widen(wg[e], wdt), widen(wu[e], wdt), widen(wd[e], wdt)
+        X = x64[ts]
+        g = X @ Wg.T
+        u = X @ Wu.T
+        h = silu(g) * u
+        y = h @ Wd.T
+        wts = routing.w[ts, js]
+        out[ts] += wts[:, None] * y          # distinct slots: (t, j) pairs are unique
+        dw[ts, js] = np.sum(d64[ts] * y, axis=1)
+        dy = wts[:, None] * d64[ts]
+        dh = dy @ Wd
+        dg = dh * u * silu_grad(g)
+        du = dh * silu(g)
+        dwd[e] = dy.T @ h
+        dwg[e] = dg.T @ X
+        dwu[e] = du.T @ X
+        np.add.at(dx, ts, dg @ Wg + du @ Wu)
+    # softmax over the selected logits
+    s = np.sum(routing.w * dw, axis=1, keepdims=True)
+    dsel = routing.w * (dw - s)
+    dl = np.zeros((T, E))
+    np.put_along_axis(dl, routing.idx.astype(np.int64), dsel, axis=1)
+    dx += dl @ wr64
+    dwr = dl.T @ x64
+    return LayerGrads(routing, disp, out, dx, dwr, dwg, dwu, dwd, dw, dl)
+
+
+# --------------------------------------------------------------------------
 # sizes and statistics printed or used on the page
 # --------------------------------------------------------------------------
 
