@@ -297,6 +297,65 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
                              int32_t* offsets, uint8_t* dropped,
                              void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Training: a forward that keeps what the backward needs, and the backward.
+ * The page gives the forward (GrokMoELayer.forward) and applies the capacity
+ * drop in training (grok_router_forward and the paragraph after it); the
+ * backward is the exact gradient of that forward by the chain rule:
+ *   - top-k selection and the capacity drop are piecewise constant: no
+ *     gradient flows through them; a dropped slot adds nothing to out and
+ *     gets no gradient;
+ *   - for a kept slot (t,j) in dispatch row r of expert e, with
+ *     g = x_t Wg_e^T, u = x_t Wu_e^T, h = silu(g) u, y = h Wd_e^T:
+ *       dw[t,j] = dout_t . y,  dy = w[t,j] dout_t,  dh = dy Wd_e,
+ *       dg = dh u silu'(g),  du = dh silu(g),
+ *       dW_down[e] += dy^T h,  dW_gate[e] += dg^T x_t,  dW_up[e] += du^T x_t,
+ *       dx_t += dg Wg_e + du Wu_e;
+ *   - softmax over the selected logits:
+ *       dlogit[t, idx[t,j]] = w[t,j] (dw[t,j] - sum_j' w[t,j'] dw[t,j']);
+ *     then dx_t += dlogit_t W_router and dW_router = dlogit^T x.
+ *
+ * Supported: act_dtype = w_dtype = MOE_BF16 (else MOE_ERR_UNSUPPORTED),
+ * T*k <= 2^22, and the shape limits above. The expert GEMMs always run on
+ * the matrix-core tiles (no decode kernels), so out may differ from
+ * moe_layer_forward's in the last bf16 bit when T <= 16.
+ *
+ * moe_layer_forward_train: the layer forward (router, dispatch with the
+ *   capacity drop, experts, combine) writing out [T,H] bf16 and the reserve:
+ *   a caller-owned device buffer of moe_layer_train_reserve_bytes(...)
+ *   bytes, 16-byte aligned. Its contents, each array starting on a 256-byte
+ *   boundary in this order: topk_idx [T,k] int32, topk_w [T,k] float32,
+ *   counts [E] int32, offsets [E+1] int32, perm [T*k] int32, slot_row [T*k]
+ *   int32, dropped [T*k] uint8 (all as moe_dispatch / moe_router_topk
+ *   define them), dispatch scratch (moe_dispatch_workspace_bytes), then the
+ *   bf16 pre-activations g [T*k,F] and u [T*k,F] (each rounded once from the
+ *   float32 accumulator), h [T*k,F] and y_perm [T*k,H] (as moe_expert_ffn
+ *   defines them). Rows at or past offsets[E] are unwritten.
+ * moe_layer_backward: given dout [T,H] bf16 (the gradient of out) and the
+ *   reserve of the forward on the same x and weights, writes
+ *   dx [T,H] bf16, dw_router [E,H] float32, dw_gate [E,F,H], dw_up [E,F,H]
+ *   and dw_down [E,H,F] bf16 (every element written; zeros for an expert
+ *   that received no rows). Float32 accumulation throughout; bf16 rounding
+ *   of the intermediates dy, dh, [dg | du] and the per-row dx, and once of
+ *   each output. ws: device scratch of moe_layer_backward_workspace_bytes
+ *   (...) bytes, 16-byte aligned (it holds the transposed weights, about
+ *   3*E*H*F*2 bytes, and the row gradients). The reserve is only read.
+ * ------------------------------------------------------------------------ */
+size_t moe_layer_train_reserve_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k);
+size_t moe_layer_backward_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k);
+moe_status moe_layer_forward_train(const void* x, moe_dtype act_dtype, const float* w_router,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
+                                   int32_t k, float capacity_factor, void* out, void* reserve,
+                                   size_t reserve_bytes, moe_stream_t stream);
+moe_status moe_layer_backward(const void* x, moe_dtype act_dtype, const float* w_router,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
+                              int32_t k, const void* dout, const void* reserve,
+                              size_t reserve_bytes, void* dx, float* dw_router, void* dw_gate,
+                              void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                              moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

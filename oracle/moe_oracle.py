@@ -397,6 +397,86 @@ def layer_backward(x: np.ndarray, act: str, wr: np.ndarray,
     return LayerGrads(routing, disp, out, dx, dwr, dwg, dwu, dwd, dw, dl)
 
 
+@dataclass
+class SampledGrads:
+    routing: Routing
+    disp: Dispatch
+    tokens: np.ndarray   # sampled tokens
+    dx: np.ndarray       # [len(tokens), H]
+    entries: dict        # name -> (indices [n,3] (e, row, col), values [n])
+
+
+def layer_backward_sampled(x: np.ndarray, act: str, wr: np.ndarray,
+                           wg: Sequence, wu: Sequence, wd: Sequence, wdt: str,
+                           dout: np.ndarray, k: int, capacity_factor, tokens: np.ndarray,
+                           entries: dict, tie_tol: float = 1e-4) -> SampledGrads:
+    """Selected outputs of layer_backward at sizes where the whole backward
+    is too slow on the CPU: dx for `tokens`, and the weight-gradient entries
+    entries[name] = [(e, i, j), ...] for name in dwg / dwu ([e][f][h]) and
+    dwd ([e][h][f]). Same formulas, evaluated per entry in float64:
+      dWd[e][h][f] = sum over e's rows r of dy_r[h] h_r[f]
+      dWg[e][f][h] = sum_r dg_r[f] x_r[h],  dWu[e][f][h] = sum_r du_r[f] x_r[h]
+    with h_r[f], dg_r[f], du_r[f] from column f of W_gate / W_up / W_down,
+    and dx_t as in layer_backward (the token's own slots and its logits).
+    Expert weights are read one expert at a time (wg[e] etc. may be lazy)."""
+    x64 = widen(x, act)
+    T, H = x64.shape
+    wr64 = np.asarray(wr, np.float32).astype(np.float64)
+    E = wr64.shape[0]
+    l32, l64 = router_logits(x64, wr)
+    routing = top_k_softmax(l32, l64, k, tie_tol)
+    disp = dispatch(routing.idx, E, capacity_factor)
+    tokens = np.asarray(tokens, np.int64)
+
+    def d64(t):
+        return np.asarray(dout[t], np.float64)
+
+    dx = np.zeros((len(tokens), H))
+    dw_tok = np.zeros((len(tokens), k))
+    vals = {n: np.zeros(len(v)) for n, v in entries.items()}
+    for e in range(E):
+        rows = range(int(disp.offsets[e]), int(disp.offsets[e + 1]))
+        slots = np.array([int(disp.perm[r]) for r in rows], np.int64)
+        mine = {n: [i for i, (ee, _, _) in enumerate(v) if ee == e] for n, v in entries.items()}
+        tok_slots = [(p, j) for p, t in enumerate(tokens) for j in range(k)
+                     if routing.idx[t, j] == e and disp.slot_row[t * k + j] >= 0]
+        if len(slots) == 0 or (not any(mine.values()) and not tok_slots):
+            continue
+        ts, js = slots // k, slots % k
+        X = x64[ts]
+        wts = routing.w[ts, js]
+        D = np.stack([d64(t) for t in ts]) if len(ts) else np.zeros((0, H))
+        dy = wts[:, None] * D
+        Wg, Wu, Wd = widen(wg[e], wdt), widen(wu[e], wdt), widen(wd[e], wdt)
+        # entries: per-column quantities over all of the expert's rows
+        for n, ids in mine.items():
+            for i in ids:
+                _, a, b = entries[n][i]
+                if n == "dwd":               # [e][h = a][f = b]
+                    g, u = X @ Wg[b], X @ Wu[b]
+                    vals[n][i] = np.sum(dy[:, a] * silu(g) * u)
+                else:                        # [e][f = a][h = b]
+                    g, u = X @ Wg[a], X @ Wu[a]
+                    dh = dy @ Wd[:, a]
+                    col = dh * u * silu_grad(g) if n == "dwg" else dh * silu(g)
+                    vals[n][i] = np.sum(col * X[:, b])
+        # the sampled tokens' own slots: whole rows
+        for p, j in tok_slots:
+            t = int(tokens[p])
+            xr = x64[t]
+            g, u = Wg @ xr, Wu @ xr
+            y = Wd @ (silu(g) * u)
+            dw_tok[p, j] = float(d64(t) @ y)
+            dh = (routing.w[t, j] * d64(t)) @ Wd
+            dx[p] += (dh * u * silu_grad(g)) @ Wg + (dh * silu(g)) @ Wu
+    for p, t in enumerate(tokens):
+        w = routing.w[t]
+        dsel = w * (dw_tok[p] - np.sum(w * dw_tok[p]))
+        dx[p] += dsel @ wr64[routing.idx[t].astype(np.int64)]
+    ent = {n: (np.asarray(v, np.int64).reshape(-1, 3), vals[n]) for n, v in entries.items()}
+    return SampledGrads(routing, disp, tokens, dx, ent)
+
+
 # --------------------------------------------------------------------------
 # sizes and statistics printed or used on the page
 # --------------------------------------------------------------------------

@@ -6,6 +6,7 @@ package is its Python binding. The library is loaded at the first call and
 its absence raises ImportError (there is no fallback path).
 """
 from .api import (  # noqa: F401
+    backward_workspace_bytes,
     layer_workspace_bytes,
     moe_combine,
     moe_dispatch,
@@ -15,8 +16,12 @@ from .api import (  # noqa: F401
     moe_expert_down,
     moe_expert_ffn,
     moe_expert_gate_up,
+    moe_layer_backward,
     moe_layer_forward,
+    moe_layer_forward_train,
     moe_router_topk,
     moe_routing_stats,
+    train_reserve_bytes,
+    train_reserve_views,
 )
 from ._lib import MoeError, LIB_PATH, load as load_library  # noqa: F401

@@ -45,6 +45,12 @@ SIGNATURES = {
     "moe_layer_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, C.c_int, C.c_int]),
     "moe_layer_forward": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _P, _P, _P, _I64, _I32,
                                     _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_train_reserve_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
+    "moe_layer_backward_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
+    "moe_layer_forward_train": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _I64, _I32, _I32,
+                                          _I32, _I32, _F, _P, _P, _SZ, _P]),
+    "moe_layer_backward": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _I64, _I32, _I32, _I32,
+                                     _I32, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

@@ -236,3 +236,95 @@ def moe_layer_forward(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Ten
         g("topk_idx"), g("topk_w"), g("counts"), g("offsets"), g("dropped"), _p(workspace),
         workspace.numel(), _stream(dev)))
     return (out, ax) if aux else out
+
+
+def train_reserve_bytes(T: int, H: int, F: int, E: int, k: int) -> int:
+    return _lib.load().moe_layer_train_reserve_bytes(T, H, F, E, k)
+
+
+def backward_workspace_bytes(T: int, H: int, F: int, E: int, k: int) -> int:
+    return _lib.load().moe_layer_backward_workspace_bytes(T, H, F, E, k)
+
+
+def _align256(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
+def train_reserve_views(reserve: torch.Tensor, T: int, H: int, F: int, E: int, k: int):
+    """Views of the arrays moe_layer_forward_train keeps in the reserve (the
+    layout include/moe.h documents): routing, dispatch, g, u, h, y_perm."""
+    N = T * k
+    disp_ws = _lib.load().moe_dispatch_workspace_bytes(T, E, k)
+    parts = [("topk_idx", torch.int32, (T, k)), ("topk_w", torch.float32, (T, k)),
+             ("counts", torch.int32, (E,)), ("offsets", torch.int32, (E + 1,)),
+             ("perm", torch.int32, (N,)), ("slot_row", torch.int32, (N,)),
+             ("dropped", torch.uint8, (N,)), ("dispatch_scratch", torch.uint8, (disp_ws,)),
+             ("g", torch.bfloat16, (N, F)), ("u", torch.bfloat16, (N, F)),
+             ("h", torch.bfloat16, (N, F)), ("y_perm", torch.bfloat16, (N, H))]
+    out, off = {}, 0
+    for name, dt, shape in parts:
+        n = 1
+        for d in shape:
+            n *= d
+        nbytes = n * torch.empty((), dtype=dt).element_size()
+        out[name] = reserve[off:off + nbytes].view(dt).view(shape)
+        off += _align256(nbytes)
+    return out
+
+
+def moe_layer_forward_train(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
+                            w_up: torch.Tensor, w_down: torch.Tensor, k: int = 2,
+                            capacity_factor: Optional[float] = None,
+                            reserve: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None):
+    """Training forward (bf16). Returns (out [T,H], reserve): the reserve
+    (uint8 device buffer) holds what moe_layer_backward reads."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.float32, 2)
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, n, torch.bfloat16, 3)
+    T, H = x.shape
+    E, F, _ = w_gate.shape
+    dev = x.device
+    nres = train_reserve_bytes(T, H, F, E, k)
+    if reserve is None or reserve.numel() < nres:
+        reserve = torch.empty(max(nres, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    check(_lib.load().moe_layer_forward_train(
+        _p(x), MOE_BF16, _p(w_router), _p(w_gate), _p(w_up), _p(w_down), MOE_BF16, T, H, F, E, k,
+        _cf(capacity_factor), _p(out), _p(reserve), reserve.numel(), _stream(dev)))
+    return out, reserve
+
+
+def moe_layer_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
+                       w_up: torch.Tensor, w_down: torch.Tensor, dout: torch.Tensor,
+                       reserve: torch.Tensor, k: int = 2,
+                       workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None):
+    """Backward of moe_layer_forward_train. Returns a dict with dx [T,H] bf16,
+    dw_router [E,H] float32, dw_gate, dw_up [E,F,H] and dw_down [E,H,F] bf16
+    (written into `grads` when given)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(dout, "dout", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.float32, 2)
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, n, torch.bfloat16, 3)
+    _need(reserve, "reserve", torch.uint8, 1)
+    T, H = x.shape
+    E, F, _ = w_gate.shape
+    dev = x.device
+    nws = backward_workspace_bytes(T, H, F, E, k)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    if grads is None:
+        grads = dict(dx=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+                     dw_router=torch.empty((E, H), dtype=torch.float32, device=dev),
+                     dw_gate=torch.empty((E, F, H), dtype=torch.bfloat16, device=dev),
+                     dw_up=torch.empty((E, F, H), dtype=torch.bfloat16, device=dev),
+                     dw_down=torch.empty((E, H, F), dtype=torch.bfloat16, device=dev))
+    check(_lib.load().moe_layer_backward(
+        _p(x), MOE_BF16, _p(w_router), _p(w_gate), _p(w_up), _p(w_down), MOE_BF16, T, H, F, E, k,
+        _p(dout), _p(reserve), reserve.numel(), _p(grads["dx"]), _p(grads["dw_router"]),
+        _p(grads["dw_gate"]), _p(grads["dw_up"]), _p(grads["dw_down"]), _p(workspace),
+        workspace.numel(), _stream(dev)))
+    return grads

@@ -141,6 +141,115 @@ LayerWs layer_ws_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E, 
   return L;
 }
 
+// The training reserve (written by moe_layer_forward_train, read by
+// moe_layer_backward); the order is part of the ABI (include/moe.h).
+struct TrainReserve {
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* slot_row;
+  uint8_t* dropped;
+  void* dws;
+  void* g;
+  void* u;
+  void* h;
+  void* y;
+  size_t total;
+};
+
+// Consecutive 256-byte-aligned pieces of one buffer (sizes only when base is NULL).
+struct Carver {
+  char* base;
+  size_t off;
+  void* take(size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+TrainReserve train_reserve_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E,
+                                  int32_t k) {
+  TrainReserve R{};
+  const int64_t N = T * k;
+  Carver c{base, 0};
+  R.idx = static_cast<int32_t*>(c.take(N * 4));
+  R.w = static_cast<float*>(c.take(N * 4));
+  R.counts = static_cast<int32_t*>(c.take(E * 4));
+  R.offsets = static_cast<int32_t*>(c.take((E + 1) * 4));
+  R.perm = static_cast<int32_t*>(c.take(N * 4));
+  R.slot_row = static_cast<int32_t*>(c.take(N * 4));
+  R.dropped = static_cast<uint8_t*>(c.take(N));
+  R.dws = c.take(dispatch_ws_bytes(T, E));
+  R.g = c.take((size_t)N * F * 2);
+  R.u = c.take((size_t)N * F * 2);
+  R.h = c.take((size_t)N * F * 2);
+  R.y = c.take((size_t)N * H * 2);
+  R.total = c.off;
+  return R;
+}
+
+// Backward scratch: transposed weights, row-layout gradients, their
+// transposes in the padded per-expert layout, and the small float32 arrays.
+struct BwdWs {
+  void* wdT;    // [E][F][H]
+  void* wguT;   // [E][H][2F]: W_gate^T then W_up^T
+  void* dy;     // [N][H]
+  void* dh;     // [N][F]
+  void* dgu;    // [N][2F]: dg then du
+  void* dxr;    // [N][H]
+  void* dyT;    // [H][Lp]
+  void* xT;     // [H][Lp]
+  void* hT;     // [F][Lp]
+  void* dguT;   // [2F][Lp]
+  float* dw;    // [N]
+  float* dl;    // [T][E]
+  float* part;  // router gradient partials
+  int64_t Lp;
+  size_t total;
+};
+
+BwdWs bwd_ws_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E, int32_t k) {
+  BwdWs B{};
+  const int64_t N = T * k;
+  const int64_t Lp = bwd_padded_rows(N, E);
+  const size_t e = (size_t)E, h = (size_t)H, f = (size_t)F;
+  Carver c{base, 0};
+  B.wdT = c.take(e * f * h * 2);
+  B.wguT = c.take(e * h * 2 * f * 2);
+  B.dy = c.take((size_t)N * h * 2);
+  B.dh = c.take((size_t)N * f * 2);
+  B.dgu = c.take((size_t)N * 2 * f * 2);
+  B.dxr = c.take((size_t)N * h * 2);
+  B.dyT = c.take(h * (size_t)Lp * 2);
+  B.xT = c.take(h * (size_t)Lp * 2);
+  B.hT = c.take(f * (size_t)Lp * 2);
+  B.dguT = c.take(2 * f * (size_t)Lp * 2);
+  B.dw = static_cast<float*>(c.take((size_t)N * 4));
+  B.dl = static_cast<float*>(c.take((size_t)T * e * 4));
+  B.part = static_cast<float*>(c.take((size_t)router_wgrad_chunks(T) * e * h * 4));
+  B.Lp = Lp;
+  B.total = c.off;
+  return B;
+}
+
+// Training: bf16 activations and weights; the padded transposed layouts are
+// addressed with 32-bit offsets within a 256-row tile.
+moe_status check_train(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k, moe_dtype act,
+                       moe_dtype wt) {
+  moe_status st;
+  if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)))
+    return st;
+  REQUIRE(act == MOE_BF16 && wt == MOE_BF16, MOE_ERR_UNSUPPORTED,
+          "training entry points support bf16 activations and weights only (got %d, %d)",
+          (int)act, (int)wt);
+  REQUIRE(T * (int64_t)k <= ((int64_t)1 << 22), MOE_ERR_UNSUPPORTED,
+          "training supports T*k <= 4194304 (got %lld)", (long long)(T * k));
+  return ok();
+}
+
 // Kernel choice: float32 -> VALU tiles; bf16 with T <= kDecodeMaxT (so at
 // most kDecodeMaxT rows per expert) -> weight-streaming decode kernels;
 // otherwise the MFMA grouped GEMM tiles.
@@ -470,6 +579,145 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
                s_up, s_down, L.h, L.y, L.fws, s);
   if (st) return st;
   return hip_status(launch_combine(L.y, L.slot_row, w, T, H, k, act, out, s), "combine launch");
+}
+
+size_t moe_layer_train_reserve_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1) return 0;
+  return train_reserve_layout(nullptr, T, H, F, E, k).total;
+}
+
+size_t moe_layer_backward_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1) return 0;
+  return bwd_ws_layout(nullptr, T, H, F, E, k).total;
+}
+
+moe_status moe_layer_forward_train(const void* x, moe_dtype act_dtype, const float* w_router,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
+                                   int32_t k, float capacity_factor, void* out, void* reserve,
+                                   size_t reserve_bytes, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_train(T, H, F, E, k, act_dtype, w_dtype))) return st;
+  REQUIRE(!std::isnan(capacity_factor), MOE_ERR_INVALID_ARGUMENT, "capacity_factor is NaN");
+  const TrainReserve need = train_reserve_layout(nullptr, T, H, F, E, k);
+  REQUIRE(reserve && reserve_bytes >= need.total && aligned16(reserve),
+          MOE_ERR_WORKSPACE_TOO_SMALL,
+          "training reserve: need %zu bytes (16-byte aligned), got %zu", need.total,
+          reserve ? reserve_bytes : (size_t)0);
+  hipStream_t s = (hipStream_t)stream;
+  TrainReserve R = train_reserve_layout(static_cast<char*>(reserve), T, H, F, E, k);
+  if (T == 0) {
+    hipError_t e = launch_fill_i32(R.counts, E, 0, s);
+    if (e == hipSuccess) e = launch_fill_i32(R.offsets, E + 1, 0, s);
+    return hip_status(e, "training forward (empty input)");
+  }
+  REQUIRE(x && w_router && w_gate && w_up && w_down && out, MOE_ERR_INVALID_ARGUMENT,
+          "x, w_router, w_gate, w_up, w_down and out must be non-NULL");
+  REQUIRE(aligned16(x) && aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) &&
+              aligned16(w_down) && aligned16(out),
+          MOE_ERR_INVALID_ARGUMENT, "x, weights and out must be 16-byte aligned");
+  hipError_t e = launch_router_topk(x, ACT_BF16, w_router, T, H, E, k, R.idx, R.w, nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "router launch");
+  const int64_t cap = capacity_of(T, k, E, capacity_factor);
+  e = launch_dispatch(R.idx, T, E, k, cap, R.counts, R.offsets, R.perm, R.slot_row, R.dropped,
+                      R.dws, s);
+  if (e != hipSuccess) return hip_status(e, "dispatch launch");
+  // the MFMA tiles at every T (the decode kernels keep no pre-activations)
+  FfnArgs a{x, R.perm, R.offsets, T, H, F, E, k, w_gate, w_up, w_down, nullptr, nullptr, nullptr,
+            R.h, R.y, nullptr, R.g, R.u};
+  e = launch_gateup_save_tiled(a, s);
+  if (e != hipSuccess) return hip_status(e, "expert gate/up launch");
+  e = launch_down_tiled(a, WT_BF16, s);
+  if (e != hipSuccess) return hip_status(e, "expert down launch");
+  return hip_status(launch_combine(R.y, R.slot_row, R.w, T, H, k, ACT_BF16, out, s),
+                    "combine launch");
+}
+
+moe_status moe_layer_backward(const void* x, moe_dtype act_dtype, const float* w_router,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
+                              int32_t k, const void* dout, const void* reserve,
+                              size_t reserve_bytes, void* dx, float* dw_router, void* dw_gate,
+                              void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                              moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_train(T, H, F, E, k, act_dtype, w_dtype))) return st;
+  REQUIRE(w_router && w_gate && w_up && w_down && dw_router && dw_gate && dw_up && dw_down,
+          MOE_ERR_INVALID_ARGUMENT, "weights and weight gradients must be non-NULL");
+  REQUIRE(aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) &&
+              aligned16(dw_router) && aligned16(dw_gate) && aligned16(dw_up) &&
+              aligned16(dw_down),
+          MOE_ERR_INVALID_ARGUMENT, "weights and weight gradients must be 16-byte aligned");
+  const TrainReserve rneed = train_reserve_layout(nullptr, T, H, F, E, k);
+  REQUIRE(reserve && reserve_bytes >= rneed.total && aligned16(reserve),
+          MOE_ERR_WORKSPACE_TOO_SMALL, "training reserve: need %zu bytes, got %zu", rneed.total,
+          reserve ? reserve_bytes : (size_t)0);
+  const BwdWs wneed = bwd_ws_layout(nullptr, T, H, F, E, k);
+  REQUIRE(ws && ws_bytes >= wneed.total && aligned16(ws), MOE_ERR_WORKSPACE_TOO_SMALL,
+          "backward workspace: need %zu bytes (16-byte aligned), got %zu", wneed.total,
+          ws ? ws_bytes : (size_t)0);
+  if (T > 0) {
+    REQUIRE(x && dout && dx, MOE_ERR_INVALID_ARGUMENT, "x, dout and dx must be non-NULL");
+    REQUIRE(aligned16(x) && aligned16(dout) && aligned16(dx), MOE_ERR_INVALID_ARGUMENT,
+            "x, dout and dx must be 16-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const TrainReserve R =
+      train_reserve_layout(static_cast<char*>(const_cast<void*>(reserve)), T, H, F, E, k);
+  const BwdWs B = bwd_ws_layout(static_cast<char*>(ws), T, H, F, E, k);
+  hipError_t e = hipSuccess;
+#define MOE_STEP(call, what) \
+  do {                       \
+    e = (call);              \
+    if (e != hipSuccess) return hip_status(e, what); \
+  } while (0)
+  // routing-weight and selected-logit gradients; dy = w * dout per kept row
+  if (T > 0)
+    MOE_STEP(launch_combine_bwd(dout, R.y, R.slot_row, R.w, R.idx, T, H, E, k, B.dy, B.dw, B.dl,
+                                s), "combine backward launch");
+  // dh = dy W_down (W_down^T as the k-contiguous operand of the down-mode GEMM)
+  MOE_STEP(launch_weight_transpose(w_down, E, H, F, B.wdT, H, 0, s), "weight transpose launch");
+  FfnArgs a1{nullptr, nullptr, R.offsets, T, F, H, E, k, nullptr, nullptr, B.wdT, nullptr, nullptr,
+             nullptr, B.dy, B.dh, nullptr, nullptr, nullptr};
+  if (T > 0) MOE_STEP(launch_down_tiled(a1, WT_BF16, s), "dh GEMM launch");
+  if (T > 0)
+    MOE_STEP(launch_swiglu_bwd(B.dh, R.g, R.u, R.offsets, E, T * k, F, B.dgu, s),
+             "SwiGLU backward launch");
+  // dx rows = [dg | du] [W_gate | W_up] (one down-mode GEMM over K = 2F)
+  MOE_STEP(launch_weight_transpose(w_gate, E, F, H, B.wguT, 2 * (int64_t)F, 0, s),
+           "weight transpose launch");
+  MOE_STEP(launch_weight_transpose(w_up, E, F, H, B.wguT, 2 * (int64_t)F, F, s),
+           "weight transpose launch");
+  FfnArgs a2{nullptr, nullptr, R.offsets, T, H, 2 * F, E, k, nullptr, nullptr, B.wguT, nullptr,
+             nullptr, nullptr, B.dgu, B.dxr, nullptr, nullptr, nullptr};
+  if (T > 0) {
+    MOE_STEP(launch_down_tiled(a2, WT_BF16, s), "dx GEMM launch");
+    MOE_STEP(launch_dx_combine(B.dxr, R.slot_row, R.idx, B.dl, w_router, T, H, E, k, dx, s),
+             "dx combine launch");
+  }
+  MOE_STEP(launch_router_wgrad(x, B.dl, T, H, E, B.part, dw_router, s), "router gradient launch");
+  // weight gradients: contractions over each expert's rows, as GEMMs over
+  // the transposed activations
+  const int64_t N = T * k;
+  if (T > 0) {
+    MOE_STEP(launch_act_transpose(B.dy, H, nullptr, k, R.offsets, E, N, H, B.dyT, B.Lp, s),
+             "transpose launch");
+    MOE_STEP(launch_act_transpose(R.h, F, nullptr, k, R.offsets, E, N, F, B.hT, B.Lp, s),
+             "transpose launch");
+    MOE_STEP(launch_act_transpose(B.dgu, 2 * (int64_t)F, nullptr, k, R.offsets, E, N, 2 * F,
+                                  B.dguT, B.Lp, s), "transpose launch");
+    MOE_STEP(launch_act_transpose(x, H, R.perm, k, R.offsets, E, N, H, B.xT, B.Lp, s),
+             "transpose launch");
+  }
+  // dW_down[e] = dy_e^T h_e: M = H, N = F; the F-row operand is the larger,
+  // so the m tiles sharing one of its blocks run together
+  const WgradArgs gd{B.dyT, B.hT, B.Lp, R.offsets, E, H, F, H, dw_down, nullptr, 1};
+  MOE_STEP(launch_wgrad(gd, s), "down weight gradient launch");
+  // [dW_gate; dW_up][e] = [dg | du]_e^T x_e: M = 2F, N = H
+  const WgradArgs ggu{B.dguT, B.xT, B.Lp, R.offsets, E, 2 * F, H, F, dw_gate, dw_up, 0};
+  MOE_STEP(launch_wgrad(ggu, s), "gate/up weight gradient launch");
+#undef MOE_STEP
+  return ok();
 }
 
 }  // extern "C"

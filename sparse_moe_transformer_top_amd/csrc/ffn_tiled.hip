@@ -95,15 +95,102 @@ MOE_DEV void block_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Modes of ffn_mfma_kernel. M_GATEUP_SAVE is M_GATEUP that also stores the
+// pre-activations g and u (bf16), which the backward reads.
+enum Mode { M_DOWN = 0, M_GATEUP = 1, M_GATEUP_SAVE = 2 };
+
+template <int WT> struct BTile {
+  static constexpr int ESZ = WT == WT_I8 ? 1 : 2;       // weight element bytes
+  static constexpr int BCH = MBK * ESZ / 16;            // 16-byte chunks per B row
+  static constexpr int LPW = MNB * BCH / 64 / MNW;      // B LDS-DMA loads per wave per stage
+};
+
+// The pipelined k loop, shared by ffn_mfma_kernel and wgrad_mfma_kernel as
+// macros over the kernel's own locals (a device function here changed the
+// forward kernel's instruction schedule): KT >= 1 stages of MBK through the
+// two-stage LDS ring SA/SB (sT0, sT1 hold the A tile then the B tile). This
+// wave's A loads read abase + aoff[j] (aptr[j] when WIDE), its B loads
+// bbase + boff[j]; arow / brow are the LDS tile rows whose MFMA operands the
+// wave reads; fa / fb hold two steps of operands; acc accumulates.
+#define MOE_ISSUE(ST, K0)                                                               \
+  do {                                                                                  \
+    const uint32_t la_ = ((ST) ? L1 : L0) + (uint32_t)(MLPW * wave) * 1024u;            \
+    const uint32_t lb_ = ((ST) ? L1 : L0) + MBM * CH * 16 + (uint32_t)(LPWB * wave) * 1024u; \
+    _Pragma("unroll") for (int j = 0; j < MLPW; ++j) {                                  \
+      if (WIDE) lds_dma16(aptr[WIDE ? j : 0] + (K0) * 2, la_ + j * 1024);               \
+      else lds_dma16(abase + (K0) * 2, aoff[j], la_ + j * 1024);                        \
+    }                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < LPWB; ++j)                                    \
+      lds_dma16(bbase + (K0) * ESZ, boff[j], lb_ + j * 1024);                           \
+  } while (0)
+#define MOE_LOADF(SLOT, ST, KS)                                                        \
+  do {                                                                                 \
+    const int chunk_ = (KS) * 2 + (lane >> 5);                                         \
+    _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) fa[SLOT][mi] = as_bf16x8(        \
+        SA[ST][arow[mi] * CH + (chunk_ ^ ((arow[mi] >> 1) & 7))]);                     \
+    if (I8) {                                                                          \
+      _Pragma("unroll") for (int s = 0; s < NI; ++s) {                                 \
+        const uint2 q_ = reinterpret_cast<const uint2*>(                               \
+            SB[ST] + brow[s] * BCH + ((KS) ^ ((brow[s] >> 2) & 3)))[lane >> 5];        \
+        fb[SLOT][s] = as_bf16x8(i8x8_to_bf16x8(q_.x, q_.y));                           \
+      }                                                                                \
+    } else {                                                                           \
+      _Pragma("unroll") for (int s = 0; s < NI; ++s) fb[SLOT][s] = as_bf16x8(          \
+          SB[ST][brow[s] * BCH + (chunk_ ^ ((brow[s] >> 1) & 7))]);                    \
+    }                                                                                  \
+  } while (0)
+// a do-while keeps the compiler from carrying a zero-trip copy of the
+// accumulators across the loop
+#define MOE_PIPELINE(KT_)                                                                 \
+  do {                                                                                    \
+    const int KT = (KT_);                                                                 \
+    MOE_ISSUE(0, 0);                                                                      \
+    if (KT > 1) MOE_ISSUE(1, MBK);                                                        \
+    if (KT > 1) wait_vmcnt<MLPW + LPWB>(); else wait_vmcnt<0>();                          \
+    block_sync();                                                                         \
+    MOE_LOADF(0, 0, 0);                                                                   \
+    int kt0 = 0;                                                                          \
+    do {                                                                                  \
+      _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                     \
+        const int kt = kt0 + u;                                                           \
+        if (kt < KT) {                                                                    \
+          _Pragma("unroll") for (int ks = 0; ks < NKS; ++ks) {                            \
+            const int slot = ks & 1;                                                      \
+            if (ks + 1 < NKS) {                                                           \
+              MOE_LOADF(slot ^ 1, u, ks + 1);                                             \
+            } else if (kt + 1 < KT) {                                                     \
+              /* stage kt+1 landed for every wave and nobody reads stage kt any */        \
+              /* more: refill stage kt's buffer with stage kt+2 */                        \
+              wait_vmcnt<0>();                                                            \
+              wait_lgkmcnt0();                                                            \
+              block_sync();                                                               \
+              if (kt + 2 < KT) MOE_ISSUE(u, (kt + 2) * MBK);                              \
+              MOE_LOADF(slot ^ 1, u ^ 1, 0);                                              \
+            }                                                                             \
+            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                             \
+              _Pragma("unroll") for (int s = 0; s < NI; ++s)                              \
+                acc[mi][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                     \
+                    fa[slot][mi], fb[slot][s], acc[mi][s], 0, 0, 0);                      \
+            /* one MFMA, then one LDS read of the next step's operands */                 \
+            _Pragma("unroll") for (int q = 0; q < MI * NI; ++q) {                         \
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          \
+              if (q < MI + NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
+            }                                                                             \
+          }                                                                               \
+        }                                                                                 \
+      }                                                                                   \
+      kt0 += 2;                                                                           \
+    } while (kt0 < KT);                                                                   \
+  } while (0)
+
 // WIDE: the gathered activation rows are addressed with 64-bit per-lane
 // pointers (x larger than 2 GiB); otherwise with 32-bit offsets from x.
-template <bool GATEUP, int WT, bool WIDE>
+template <int MODE, int WT, bool WIDE>
 __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t n_ntiles) {
+  constexpr bool GATEUP = MODE == M_GATEUP || MODE == M_GATEUP_SAVE;
   constexpr bool I8 = WT == WT_I8;
-  constexpr int ESZ = I8 ? 1 : 2;               // weight element bytes
+  constexpr int ESZ = BTile<WT>::ESZ, BCH = BTile<WT>::BCH, LPWB = BTile<WT>::LPW;
   constexpr int CH = MBK / 8;                   // 16-byte chunks per A row (bf16)
-  constexpr int BCH = MBK * ESZ / 16;           // 16-byte chunks per B row (int8 or bf16)
-  constexpr int LPWB = MNB * BCH / 64 / MNW;    // B LDS-DMA loads per wave per stage
   constexpr int MWM = WaveGrid<WT>::M, MWN = WaveGrid<WT>::N;
   constexpr int MW = MBM / MWM, NWR = MNB / MWN;
   constexpr int MI = MW / 32, NI = NWR / 32;    // 8 accumulators: 2 x 4 (bf16) or 4 x 2 (int8)
@@ -187,81 +274,8 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
       for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
   bf16x8 fa[2][MI], fb[2][NI];
 
-#define MOE_ISSUE(ST, K0)                                                               \
-  do {                                                                                  \
-    const uint32_t la_ = ((ST) ? L1 : L0) + (uint32_t)(MLPW * wave) * 1024u;            \
-    const uint32_t lb_ = ((ST) ? L1 : L0) + MBM * CH * 16 + (uint32_t)(LPWB * wave) * 1024u; \
-    _Pragma("unroll") for (int j = 0; j < MLPW; ++j) {                                  \
-      if (WIDE) lds_dma16(aptr[WIDE ? j : 0] + (K0) * 2, la_ + j * 1024);               \
-      else lds_dma16(abase + (K0) * 2, aoff[j], la_ + j * 1024);                        \
-    }                                                                                   \
-    _Pragma("unroll") for (int j = 0; j < LPWB; ++j)                                    \
-      lds_dma16(bbase + (K0) * ESZ, boff[j], lb_ + j * 1024);                           \
-  } while (0)
-#define MOE_LOADF(SLOT, ST, KS)                                                        \
-  do {                                                                                 \
-    const int chunk_ = (KS) * 2 + (lane >> 5);                                         \
-    _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) fa[SLOT][mi] = as_bf16x8(        \
-        SA[ST][arow[mi] * CH + (chunk_ ^ ((arow[mi] >> 1) & 7))]);                     \
-    if (I8) {                                                                          \
-      _Pragma("unroll") for (int s = 0; s < NI; ++s) {                                 \
-        const uint2 q_ = reinterpret_cast<const uint2*>(                               \
-            SB[ST] + brow[s] * BCH + ((KS) ^ ((brow[s] >> 2) & 3)))[lane >> 5];        \
-        fb[SLOT][s] = as_bf16x8(i8x8_to_bf16x8(q_.x, q_.y));                           \
-      }                                                                                \
-    } else {                                                                           \
-      _Pragma("unroll") for (int s = 0; s < NI; ++s) fb[SLOT][s] = as_bf16x8(          \
-          SB[ST][brow[s] * BCH + (chunk_ ^ ((brow[s] >> 1) & 7))]);                    \
-    }                                                                                  \
-  } while (0)
-
-  // K >= 64, so there is at least one stage; a do-while keeps the compiler
-  // from carrying a zero-trip copy of the accumulators across the loop
-  const int KT = K / MBK;
-  MOE_ISSUE(0, 0);
-  if (KT > 1) MOE_ISSUE(1, MBK);
-  if (KT > 1) wait_vmcnt<MLPW + LPWB>(); else wait_vmcnt<0>();
-  block_sync();
-  MOE_LOADF(0, 0, 0);
-  int kt0 = 0;
-  do {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kt = kt0 + u;
-      if (kt < KT) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int slot = ks & 1;
-          if (ks + 1 < NKS) {
-            MOE_LOADF(slot ^ 1, u, ks + 1);
-          } else if (kt + 1 < KT) {
-            // stage kt+1 landed for every wave and nobody reads stage kt any
-            // more: refill stage kt's buffer with stage kt+2
-            wait_vmcnt<0>();
-            wait_lgkmcnt0();
-            block_sync();
-            if (kt + 2 < KT) MOE_ISSUE(u, (kt + 2) * MBK);
-            MOE_LOADF(slot ^ 1, u ^ 1, 0);
-          }
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int s = 0; s < NI; ++s)
-              acc[mi][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][s],
-                                                                   acc[mi][s], 0, 0, 0);
-          // one MFMA, then one LDS read of the next step's operands
-#pragma unroll
-          for (int q = 0; q < MI * NI; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (q < MI + NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        }
-      }
-    }
-    kt0 += 2;
-  } while (kt0 < KT);
-#undef MOE_ISSUE
-#undef MOE_LOADF
+  // K >= 64, so there is at least one stage
+  MOE_PIPELINE(K / MBK);
 
   // epilogue; 32x32 accumulator layout: lane l holds column l%32, register
   // v holds row 8*(v/4) + 4*(l/32) + v%4
@@ -284,6 +298,10 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
               u *= a.su[(int64_t)e * a.F + n];
             }
             hrow[n] = f32_to_bf16_bits(swiglu(g, u));
+            if (MODE == M_GATEUP_SAVE) {
+              static_cast<uint16_t*>(a.g_save)[(int64_t)r * a.F + n] = f32_to_bf16_bits(g);
+              static_cast<uint16_t*>(a.u_save)[(int64_t)r * a.F + n] = f32_to_bf16_bits(u);
+            }
           }
         }
       } else {
@@ -300,14 +318,116 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   }
 }
 
-template <bool GATEUP, int WT, bool WIDE>
+template <int MODE, int WT, bool WIDE>
 hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
+  constexpr bool GATEUP = MODE != M_DOWN;
   const uint32_t nt = GATEUP ? (uint32_t)((a.F + MNB / 2 - 1) / (MNB / 2))
                              : (uint32_t)((a.H + MNB - 1) / MNB);
-  hipLaunchKernelGGL((ffn_mfma_kernel<GATEUP, WT, WIDE>),
+  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WT, WIDE>),
                      dim3(grouped_grid(a.T * a.k, a.E, MBM, nt)), dim3(MNW * 64), 0, s, a, nt);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// weight gradients of the backward: per expert e,
+//   C_e[m][n] = sum over k in [p_e, p_(e+1)) of A[m][k] * B[n][k]
+// with A [M][ld] and B [N][ld] the transposed activations (token rows as k),
+// each expert's k range padded with zeros to a multiple of MBK (p_e is the
+// padded exclusive scan of the expert row counts, so every stage is whole).
+// Rows m < m_split go to out0 [E][m_split][N], the rest to out1
+// [E][M - m_split][N], bf16. Tiles: MT x NT per expert; a group of tiles
+// that share one operand block (the MT m tiles of one n tile when m_fast,
+// else the NT n tiles of one m tile) stays on one XCD, and the XCDs take
+// groups in turn, so a heavy expert is spread over all of them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(MNW * 64) void wgrad_mfma_kernel(WgradArgs w) {
+  constexpr bool I8 = false, WIDE = false;
+  constexpr int CH = MBK / 8, NKS = MBK / 16;
+  constexpr int ESZ = 2, BCH = BTile<WT_BF16>::BCH, LPWB = BTile<WT_BF16>::LPW;
+  constexpr int MWM = WaveGrid<WT_BF16>::M, MWN = WaveGrid<WT_BF16>::N;
+  constexpr int MW = MBM / MWM, NWR = MNB / MWN;
+  constexpr int MI = MW / 32, NI = NWR / 32;
+  __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
+  u32x4* const SA[2] = {sT0, sT1};
+  u32x4* const SB[2] = {sT0 + MBM * CH, sT1 + MBM * CH};
+  const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
+  const char* const* aptr = nullptr;
+
+  const uint32_t MT = (uint32_t)(w.M + MBM - 1) / MBM, NT = (uint32_t)(w.N + MNB - 1) / MNB;
+  const uint32_t G = w.m_fast ? MT : NT;
+  const uint32_t slot = blockIdx.x >> 3;
+  const uint32_t lin = ((slot / G) * 8 + (blockIdx.x & 7)) * G + slot % G;
+  if (lin >= (uint32_t)w.E * MT * NT) return;
+  const int e = (int)(lin / (MT * NT));
+  const uint32_t rem = lin % (MT * NT);
+  const int mt = (int)(w.m_fast ? rem % MT : rem / NT);
+  const int nt = (int)(w.m_fast ? rem / MT : rem % NT);
+  const int m0 = mt * MBM, n0 = nt * MNB;
+  const int p0 = __builtin_amdgcn_readfirstlane(padded_start(w.offsets, e, MBK));
+  const int kt = (w.offsets[e + 1] - w.offsets[e] + MBK - 1) / MBK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const char* const abase =
+      uniform_ptr(static_cast<const char*>(w.a) + ((int64_t)m0 * w.ld + p0) * 2);
+  const char* const bbase =
+      uniform_ptr(static_cast<const char*>(w.b) + ((int64_t)n0 * w.ld + p0) * 2);
+  uint32_t aoff[MLPW], boff[LPWB];
+#pragma unroll
+  for (int j = 0; j < MLPW; ++j) {
+    const int q = (MLPW * wave + j) * 64 + lane;
+    const int r = q / CH, c = (q % CH) ^ ((r >> 1) & 7);
+    aoff[j] = (uint32_t)(min(m0 + r, w.M - 1) - m0) * (uint32_t)(w.ld * 2) + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < LPWB; ++j) {
+    const int q = (LPWB * wave + j) * 64 + lane;
+    const int r = q / BCH, c = (q % BCH) ^ ((r >> 1) & 7);
+    boff[j] = (uint32_t)(min(n0 + r, w.N - 1) - n0) * (uint32_t)(w.ld * 2) + c * 16;
+  }
+  const int wm = wave / MWN, wn = wave % MWN;
+  int arow[MI], brow[NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) arow[mi] = wm * MW + mi * 32 + (lane & 31);
+#pragma unroll
+  for (int s = 0; s < NI; ++s) brow[s] = wn * NWR + s * 32 + (lane & 31);
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int s = 0; s < NI; ++s)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
+
+  bf16x8 fa[2][MI], fb[2][NI];
+
+  // an expert without rows has a zero gradient: no stage, zeros written
+  if (kt > 0) MOE_PIPELINE(kt);
+
+  const int jcol = lane & 31;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + wm * MW + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (m >= w.M) continue;
+      uint16_t* const crow =
+          m < w.m_split
+              ? static_cast<uint16_t*>(w.out0) + ((int64_t)e * w.m_split + m) * w.N
+              : static_cast<uint16_t*>(w.out1) +
+                    ((int64_t)e * (w.M - w.m_split) + (m - w.m_split)) * w.N;
+#pragma unroll
+      for (int s = 0; s < NI; ++s) {
+        const int n = n0 + wn * NWR + s * 32 + jcol;
+        if (n < w.N) crow[n] = f32_to_bf16_bits(acc[mi][s][v]);
+      }
+    }
+  }
+}
+
+#undef MOE_PIPELINE
+#undef MOE_ISSUE
+#undef MOE_LOADF
 
 // 32-bit offsets from x reach the gathered rows while x is below 2 GiB
 bool x_needs_wide(const FfnArgs& a) { return (uint64_t)a.T * (uint64_t)a.H * 2 > (1ull << 31); }
@@ -323,16 +443,33 @@ size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt) {
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
   if (wt == WT_I4) return hipErrorNotSupported;   // int4: decode kernels only
   if (x_needs_wide(a))
-    return wt == WT_I8 ? launch_mfma<true, WT_I8, true>(a, s)
-                       : launch_mfma<true, WT_BF16, true>(a, s);
-  return wt == WT_I8 ? launch_mfma<true, WT_I8, false>(a, s)
-                     : launch_mfma<true, WT_BF16, false>(a, s);
+    return wt == WT_I8 ? launch_mfma<M_GATEUP, WT_I8, true>(a, s)
+                       : launch_mfma<M_GATEUP, WT_BF16, true>(a, s);
+  return wt == WT_I8 ? launch_mfma<M_GATEUP, WT_I8, false>(a, s)
+                     : launch_mfma<M_GATEUP, WT_BF16, false>(a, s);
 }
 
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
   if (wt == WT_I4) return hipErrorNotSupported;
-  return wt == WT_I8 ? launch_mfma<false, WT_I8, false>(a, s)
-                     : launch_mfma<false, WT_BF16, false>(a, s);
+  return wt == WT_I8 ? launch_mfma<M_DOWN, WT_I8, false>(a, s)
+                     : launch_mfma<M_DOWN, WT_BF16, false>(a, s);
+}
+
+hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s) {
+  return x_needs_wide(a) ? launch_mfma<M_GATEUP_SAVE, WT_BF16, true>(a, s)
+                         : launch_mfma<M_GATEUP_SAVE, WT_BF16, false>(a, s);
+}
+
+unsigned wgrad_grid(const WgradArgs& w) {
+  const unsigned MT = (unsigned)(w.M + MBM - 1) / MBM, NT = (unsigned)(w.N + MNB - 1) / MNB;
+  const unsigned G = w.m_fast ? MT : NT;
+  const unsigned groups = (unsigned)w.E * MT * NT / G;
+  return (groups + 7) / 8 * 8 * G;
+}
+
+hipError_t launch_wgrad(const WgradArgs& w, hipStream_t s) {
+  hipLaunchKernelGGL(wgrad_mfma_kernel, dim3(wgrad_grid(w)), dim3(MNW * 64), 0, s, w);
+  return hipGetLastError();
 }
 
 }  // namespace moe

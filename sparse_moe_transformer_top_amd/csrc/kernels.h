@@ -44,6 +44,8 @@ struct FfnArgs {
   void* h;                // [T*k,F] act
   void* y;                // [T*k,H] act
   void* ws;
+  void* g_save;           // [T*k,F] bf16 pre-activations (launch_gateup_save_tiled only)
+  void* u_save;           // [T*k,F]
 };
 
 // largest T for which the decode (few rows per expert) kernels are used
@@ -62,6 +64,23 @@ hipError_t launch_gateup_f32(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_f32(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
+// bf16 gate/up that also writes g_save and u_save (training forward)
+hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s);
+
+// Backward weight-gradient GEMM (ffn_tiled.hip), bf16: per expert e,
+// C_e[m][n] = sum over the expert's padded k range of a[m][k] * b[n][k].
+struct WgradArgs {
+  const void* a;          // [M][ld]
+  const void* b;          // [N][ld]
+  int64_t ld;             // elements per row of a and b (256 * ld * 2 < 2^32)
+  const int32_t* offsets; // [E+1] dispatch offsets; expert e's k range starts
+                          // at the exclusive scan of the counts rounded up to 64
+  int E, M, N, m_split;
+  void* out0;             // [E][m_split][N] bf16
+  void* out1;             // [E][M - m_split][N] bf16 (unused when m_split == M)
+  int m_fast;             // 1: tiles sharing a B block run together
+};
+hipError_t launch_wgrad(const WgradArgs& w, hipStream_t s);
 size_t decode_ws_bytes(int64_t T, int H, int k);
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
@@ -69,6 +88,32 @@ hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 // routing statistics (stats.hip)
 hipError_t launch_routing_stats(const float* logits, const int32_t* counts, int64_t T, int E,
                                 int k, float* util, float* margin, float* mass, hipStream_t s);
+
+// backward of the layer (bwd.hip), bf16 activations and weights
+// rows of the padded per-expert layout of n_rows dispatch rows (each expert's
+// segment rounded up to 64; this bound holds for any split of the rows)
+int64_t bwd_padded_rows(int64_t n_rows, int E);
+int64_t router_wgrad_chunks(int64_t T);
+// dst[e][c][col0 + r] = src[e][r][c] for E matrices [R][C] (R, C multiples of 64)
+hipError_t launch_weight_transpose(const void* src, int E, int R, int C, void* dst, int64_t ldd,
+                                   int col0, hipStream_t s);
+// dst[c][p] (row stride ldd) for the padded layout of the dispatch rows; the
+// source row of dispatch row r is src + r*lds, or src + (perm[r]/k)*lds when
+// perm is given. C a multiple of 64.
+hipError_t launch_act_transpose(const void* src, int64_t lds, const int32_t* perm, int k,
+                                const int32_t* offsets, int E, int64_t n_rows, int C, void* dst,
+                                int64_t ldd, hipStream_t s);
+hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* slot_row,
+                              const float* w, const int32_t* idx, int64_t T, int H, int E, int k,
+                              void* dy, float* dw, float* dl, hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* dh, const void* g, const void* u, const int32_t* offsets,
+                             int E, int64_t max_rows, int F, void* dgu, hipStream_t s);
+hipError_t launch_dx_combine(const void* dxr, const int32_t* slot_row, const int32_t* idx,
+                             const float* dl, const float* wr, int64_t T, int H, int E, int k,
+                             void* dx, hipStream_t s);
+// part: router_wgrad_chunks(T) * E * H floats
+hipError_t launch_router_wgrad(const void* x, const float* dl, int64_t T, int H, int E,
+                               float* part, float* dwr, hipStream_t s);
 
 // expert-parallel layouts (ep.hip)
 hipError_t launch_ep_pack(const void* x, int64_t row_bytes, const int32_t* perm,

@@ -14,6 +14,7 @@ SwiGLU at scale" for the expert weight shapes, stored as nn.Linear [out, in]).
 from .configs import LayerConfig, CONFIGS, PARITY_CONFIGS, get_config  # noqa: F401
 from .gen import (  # noqa: F401
     routing_logits,
+    grad_output,
     HostInputs,
     generate_host,
     bf16_bits_from_f32,

@@ -69,6 +69,10 @@ CONFIGS = {
         "capacity", T=16384, H=6144, F=32768, capacity_factor=1.25,
         wdt="i8", skew=SKEW_T16384,
         description="capacity 1.25, int8 weights with per-row fp32 scales, skewed router, T=16384"),
+    "train": LayerConfig(
+        "train", T=8192, H=6144, F=32768, capacity_factor=1.25,
+        description="Grok-1 shape training step (forward keeping activations + backward): "
+                    "one 8192-token batch, bf16, capacity 1.25"),
     "decode_i4": LayerConfig(
         "decode_i4", T=8, H=6144, F=32768, wdt="i4",
         description="Grok-1 shape decode with int4 weights (one fp32 scale per row and 128 k): "

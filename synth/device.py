@@ -117,3 +117,9 @@ def generate_device(cfg: LayerConfig, device="cuda", seed: Optional[int] = None,
                 sdst[e].copy_(s)
             del w32, q
     return DeviceInputs(cfg, x, wr, wg, wu, wd, sg, su, sd)
+
+
+def grad_output_device(T: int, H: int, seed: int, device="cuda") -> torch.Tensor:
+    """Seeded gradient of the layer output [T,H] ~ N(0,1) in bf16 (index 10^6
+    keeps its stream apart from the layer inputs')."""
+    return _randn((T, H), 1.0, device, seed, 1_000_000).to(torch.bfloat16)

@@ -167,3 +167,9 @@ def routing_logits(T: int, E: int, seed: int, tie_frac: float = 0.3) -> np.ndarr
     ints = rng.integers(-2, 3, (T, E)).astype(np.float64)
     return np.where(rng.random((T, E)) < tie_frac, ints, g).astype(np.float32)
 
+
+
+def grad_output(T: int, H: int, seed: int) -> np.ndarray:
+    """Seeded gradient of the layer output [T,H] ~ N(0,1), as bf16 bits."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return bf16_bits_from_f32(rng.standard_normal((T, H), dtype=np.float32))

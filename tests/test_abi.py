@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -194,3 +194,56 @@ def test_workspace_sizes(lib):
     assert lib.moe_layer_workspace_bytes(T, H, F, E, k, F32, F32) > n
     assert lib.moe_layer_workspace_bytes(0, H, F, E, k, BF16, BF16) > 0
     assert lib.moe_expert_ffn_workspace_bytes(T, H, F, E, k, BF16, BF16) >= 0
+
+
+def fwd_train(lib, T=32, H=128, F=256, E=8, k=2, act=BF16, wdt=BF16, cf=0.0, res=P, nres=None,
+              out=P, x=P):
+    nres = lib.moe_layer_train_reserve_bytes(T, H, F, E, k) if nres is None else nres
+    return lib.moe_layer_forward_train(x, act, P, P, P, P, wdt, T, H, F, E, k, cf, out, res, nres,
+                                       None)
+
+
+def bwd(lib, T=32, H=128, F=256, E=8, k=2, act=BF16, wdt=BF16, res=P, nres=None, ws=P, nws=None,
+        dx=P, dwr=P, dout=P):
+    nres = lib.moe_layer_train_reserve_bytes(T, H, F, E, k) if nres is None else nres
+    nws = lib.moe_layer_backward_workspace_bytes(T, H, F, E, k) if nws is None else nws
+    return lib.moe_layer_backward(P, act, P, P, P, P, wdt, T, H, F, E, k, dout, res, nres, dx, dwr,
+                                  P, P, P, ws, nws, None)
+
+
+def test_training_argument_errors(lib):
+    assert fwd_train(lib, out=None) == INV
+    assert fwd_train(lib, x=MIS) == INV
+    assert fwd_train(lib, nres=64) == WS
+    assert fwd_train(lib, res=None) == WS
+    assert fwd_train(lib, res=MIS) == WS
+    assert fwd_train(lib, cf=math.nan) == INV
+    assert fwd_train(lib, act=F32, wdt=F32) == UNS       # bf16 only
+    assert fwd_train(lib, wdt=I8) == UNS
+    assert fwd_train(lib, H=96) == UNS
+    assert fwd_train(lib, T=2 ** 22, k=2) == UNS          # T*k above 2^22
+    assert bwd(lib, dx=None) == INV
+    assert bwd(lib, dout=MIS) == INV
+    assert bwd(lib, dwr=None) == INV
+    assert bwd(lib, nres=64) == WS
+    assert bwd(lib, nws=64) == WS
+    assert bwd(lib, ws=None) == WS
+    assert bwd(lib, act=F32, wdt=F32) == UNS
+    assert bwd(lib, k=5, E=8) == UNS
+    assert bwd(lib, E=17) == UNS
+
+
+def test_training_sizes(lib):
+    T, H, F, E, k = 8192, 6144, 32768, 8, 2
+    N = T * k
+    r = lib.moe_layer_train_reserve_bytes(T, H, F, E, k)
+    # g, u, h [N, F] and y_perm [N, H] in bf16 dominate the reserve
+    assert N * (3 * F + H) * 2 <= r < N * (3 * F + H) * 2 + 16 * 2 ** 20
+    w = lib.moe_layer_backward_workspace_bytes(T, H, F, E, k)
+    # transposed weights (3 E H F bf16) plus the row gradients and their
+    # padded transposes
+    Lp = (N + 63 * E + 63) // 64 * 64
+    rows = N * (H + F + 2 * F + H) * 2 + Lp * (H + H + F + 2 * F) * 2
+    assert 3 * E * H * F * 2 + rows <= w < 3 * E * H * F * 2 + rows + 64 * 2 ** 20
+    assert lib.moe_layer_train_reserve_bytes(0, H, F, E, k) > 0
+    assert lib.moe_layer_backward_workspace_bytes(-1, H, F, E, k) == 0

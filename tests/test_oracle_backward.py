@@ -174,3 +174,29 @@ def test_silu_grad_closed_form():
     h = 1e-5
     fd = (oracle.silu(g + h) - oracle.silu(g - h)) / (2 * h)
     assert np.allclose(oracle.silu_grad(g), fd, rtol=1e-8, atol=1e-10)
+
+
+@pytest.mark.parametrize("cf", [None, 1.0])
+def test_sampled_backward_equals_full(cf):
+    # the per-entry evaluation used at sizes the full backward cannot reach
+    cfg = _cfg(T=50, H=32, F=64, E=8, k=2, cf=cf, act="bf16", wdt="bf16", seed=21)
+    inp = synth.generate_host(cfg)
+    dout = synth.grad_output(cfg.T, cfg.H, seed=4)
+    d64 = oracle.widen(dout, "bf16")
+    g = oracle.layer_backward(inp.x, "bf16", inp.wr, inp.wg, inp.wu, inp.wd, "bf16", d64,
+                              k=2, capacity_factor=cf)
+    rng = np.random.default_rng(0)
+    ent = {"dwg": [(int(rng.integers(8)), int(rng.integers(64)), int(rng.integers(32)))
+                   for _ in range(20)],
+           "dwu": [(int(rng.integers(8)), int(rng.integers(64)), int(rng.integers(32)))
+                   for _ in range(20)],
+           "dwd": [(int(rng.integers(8)), int(rng.integers(32)), int(rng.integers(64)))
+                   for _ in range(20)]}
+    tokens = np.array([0, 7, 19, 49])
+    s = oracle.layer_backward_sampled(inp.x, "bf16", inp.wr, inp.wg, inp.wu, inp.wd, "bf16",
+                                      dout=d64, k=2, capacity_factor=cf, tokens=tokens,
+                                      entries=ent)
+    assert np.allclose(s.dx, g.dx[tokens], rtol=1e-12, atol=1e-12)
+    for n, full in (("dwg", g.dwg), ("dwu", g.dwu), ("dwd", g.dwd)):
+        ids, v = s.entries[n]
+        assert np.allclose(v, full[ids[:, 0], ids[:, 1], ids[:, 2]], rtol=1e-12, atol=1e-13)
