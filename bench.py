@@ -14,6 +14,9 @@ line on stdout (logs go to stderr):
              its mean duration, timed with events around that launch in a
              stage-by-stage pass over K more steps;
   prefill    the same layer at T = 8192 (one full context), MFMA-bound;
+  train      a training step on the same weights at T = 8192 with capacity
+             1.25: moe_layer_forward_train + moe_layer_backward, tokens/s,
+             stage times and the weight-gradient GEMM against bf16 MFMA peak;
   cpu_baseline  the oracle (numpy float64, test infrastructure) on a bounded
              sample of the same workload on this host's cores.
 """
@@ -191,6 +194,96 @@ class Layer:
         return out[0], out[1], n
 
 
+class TrainStep:
+    """One training step of the layer: moe_layer_forward_train, then
+    moe_layer_backward for a seeded output gradient, on the given weights."""
+
+    def __init__(self, cfg, dev, torch, moe, weights):
+        from synth.device import generate_device, grad_output_device
+        self.cfg, self.torch, self.moe = cfg, torch, moe
+        xd = generate_device(cfg, dev, x_only=True)
+        self.d = type(weights)(cfg, xd.x, xd.wr, weights.wg, weights.wu, weights.wd,
+                               None, None, None)
+        T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
+        self.dout = grad_output_device(T, H, seed=cfg.seed, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.res = torch.empty(moe.train_reserve_bytes(T, H, F, E, k), **u8)
+        self.ws = torch.empty(moe.backward_workspace_bytes(T, H, F, E, k), **u8)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        d = self.d
+        self.grads = dict(dx=torch.empty_like(d.x),
+                          dw_router=torch.empty((E, H), dtype=torch.float32, device=dev),
+                          dw_gate=torch.empty_like(d.wg), dw_up=torch.empty_like(d.wu),
+                          dw_down=torch.empty_like(d.wd))
+
+    def forward(self):
+        d, c = self.d, self.cfg
+        self.moe.moe_layer_forward_train(d.x, d.wr, d.wg, d.wu, d.wd, k=c.k,
+                                         capacity_factor=c.capacity_factor, reserve=self.res,
+                                         out=self.out)
+
+    def backward(self, split=False):
+        d, c = self.d, self.cfg
+        self.moe.moe_layer_backward(d.x, d.wr, d.wg, d.wu, d.wd, self.dout, self.res, k=c.k,
+                                    workspace=self.ws, grads=self.grads, split=split)
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.forward()
+            self.backward()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            self.forward()
+            self.backward()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def stage_times(self, steps):
+        """Mean ms of the forward, the backward's data step and its weight
+        step (the two launches of the weight-gradient GEMM), with events
+        between the calls on torch's current stream (the library's stream)."""
+        torch, moe, d, c = self.torch, self.moe, self.d, self.cfg
+        evs = []
+        for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            self.forward()
+            ev[1].record()
+            moe.moe_layer_backward(d.x, d.wr, d.wg, d.wu, d.wd, self.dout, self.res, k=c.k,
+                                   workspace=self.ws, grads=self.grads, split=True)
+            ev[2].record()
+            evs.append(ev)
+        torch.cuda.synchronize()
+        fw = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        bw = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        # the weight step on its own, behind a device-side delay so that the
+        # events bracket the two GEMM launches and not the host
+        wt = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(2_000_000)
+            a.record()
+            self.weights_step()
+            b.record()
+            torch.cuda.synchronize()
+            wt.append(a.elapsed_time(b))
+        return fw, bw, sum(wt) / steps
+
+    def weights_step(self):
+        c = self.cfg
+        self.moe.moe_layer_backward_weights(self.res, self.ws, self.grads, c.T, c.H, c.F, c.E,
+                                            c.k)
+
+    def kept_rows(self):
+        v = self.moe.train_reserve_views(self.res, self.cfg.T, self.cfg.H, self.cfg.F,
+                                         self.cfg.E, self.cfg.k)
+        return int(v["offsets"][-1].item())
+
+
 def cpu_baseline(layer, n_tokens):
     """The oracle on the first n_tokens tokens of the workload (routing and
     dispatch over all T tokens, expert FFN and combine for the sample)."""
@@ -241,6 +334,7 @@ def main():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "capacity", "decode_i4"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill secondary line")
+    ap.add_argument("--no-train", action="store_true", help="skip the training-step secondary line")
     ap.add_argument("--cpu-tokens", type=int, default=8,
                     help="tokens in the oracle's timed sample (0 skips the CPU baseline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -370,6 +464,35 @@ def main():
             "pack_GBps": round(pbytes / (ppk * 1e-3) / 1e9, 1), "unpack_us": round(pup * 1e3, 1),
             "unpack_GBps": round(pbytes / (pup * 1e-3) / 1e9, 1)}
         del pl
+        torch.cuda.empty_cache()
+
+    if not args.no_train and cfg.name == "decode":
+        tcfg = synth.CONFIGS["train"]
+        log("training step: same weights, T=8192 tokens, capacity 1.25")
+        tr = TrainStep(tcfg, dev, torch, moe, layer.d)
+        nsteps = max(3, args.steps // 4)
+        tms = tr.timed(nsteps, 2)
+        fw, bw, wt = tr.stage_times(nsteps)
+        nk = tr.kept_rows()
+        # flops: forward 6 n H F; backward 12 n H F (dh 2, dx 4, dW_down 2,
+        # dW_gate|dW_up 4); the weight step's two launches hold 6 n H F
+        tflops = 18.0 * H * F * nk
+        wflops = 6.0 * H * F * nk
+        wach = wflops / (wt * 1e-3) / 1e12
+        result["train"] = {
+            "workload": f"train: {tcfg.description}", "tokens_per_s": round(tcfg.T / (tms * 1e-3), 1),
+            "ms_per_step": round(tms, 3), "kept_rows": nk,
+            "TFLOPs": round(tflops / (tms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(tflops / (tms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "stages_ms": {"forward_train": round(fw, 3), "backward": round(bw, 3),
+                          "backward_weights": round(wt, 3)},
+            "roofline": {"bound": "mfma", "kernel": "wgrad_mfma_kernel (dW_down, then "
+                         "dW_gate|dW_up: 2 launches per step)",
+                         "achieved": round(wach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(wach / BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops": wflops / 2, "mean_ms": round(wt / 2, 4),
+                         "traffic": None}}
+        del tr
         torch.cuda.empty_cache()
 
     if args.cpu_tokens > 0:

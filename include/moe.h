@@ -340,6 +340,13 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
  *   each output. ws: device scratch of moe_layer_backward_workspace_bytes
  *   (...) bytes, 16-byte aligned (it holds the transposed weights, about
  *   3*E*H*F*2 bytes, and the row gradients). The reserve is only read.
+ * moe_layer_backward is exactly moe_layer_backward_data followed by
+ *   moe_layer_backward_weights on one stream with the same reserve and ws:
+ *   the data step writes dx and dw_router and leaves in ws what the weight
+ *   step reads (so a schedule may run the weight step later, as long as ws
+ *   and the reserve are left untouched in between); the weight step writes
+ *   dw_gate, dw_up and dw_down and reads only ws and the reserve's dispatch
+ *   offsets (neither x nor the weights).
  * ------------------------------------------------------------------------ */
 size_t moe_layer_train_reserve_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k);
 size_t moe_layer_backward_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k);
@@ -355,6 +362,16 @@ moe_status moe_layer_backward(const void* x, moe_dtype act_dtype, const float* w
                               size_t reserve_bytes, void* dx, float* dw_router, void* dw_gate,
                               void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
                               moe_stream_t stream);
+moe_status moe_layer_backward_data(const void* x, moe_dtype act_dtype, const float* w_router,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
+                                   int32_t k, const void* dout, const void* reserve,
+                                   size_t reserve_bytes, void* dx, float* dw_router, void* ws,
+                                   size_t ws_bytes, moe_stream_t stream);
+moe_status moe_layer_backward_weights(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                                      const void* reserve, size_t reserve_bytes, void* dw_gate,
+                                      void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     moe_expert_ffn,
     moe_expert_gate_up,
     moe_layer_backward,
+    moe_layer_backward_weights,
     moe_layer_forward,
     moe_layer_forward_train,
     moe_router_topk,

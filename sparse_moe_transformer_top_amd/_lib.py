@@ -51,6 +51,10 @@ SIGNATURES = {
                                           _I32, _I32, _F, _P, _P, _SZ, _P]),
     "moe_layer_backward": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _I64, _I32, _I32, _I32,
                                      _I32, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_backward_data": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _I64, _I32, _I32,
+                                          _I32, _I32, _P, _P, _SZ, _P, _P, _P, _SZ, _P]),
+    "moe_layer_backward_weights": (C.c_int, [_I64, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P, _P,
+                                             _P, _SZ, _P]),
 }
 
 _lib = None

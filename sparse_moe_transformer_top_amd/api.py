@@ -300,10 +300,12 @@ def moe_layer_forward_train(x: torch.Tensor, w_router: torch.Tensor, w_gate: tor
 def moe_layer_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
                        w_up: torch.Tensor, w_down: torch.Tensor, dout: torch.Tensor,
                        reserve: torch.Tensor, k: int = 2,
-                       workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None):
+                       workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
+                       split: bool = False):
     """Backward of moe_layer_forward_train. Returns a dict with dx [T,H] bf16,
     dw_router [E,H] float32, dw_gate, dw_up [E,F,H] and dw_down [E,H,F] bf16
-    (written into `grads` when given)."""
+    (written into `grads` when given). split=True makes the same computation
+    as two calls, moe_layer_backward_data then moe_layer_backward_weights."""
     _need(x, "x", torch.bfloat16, 2)
     _need(dout, "dout", torch.bfloat16, 2)
     _need(w_router, "w_router", torch.float32, 2)
@@ -322,9 +324,33 @@ def moe_layer_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Te
                      dw_gate=torch.empty((E, F, H), dtype=torch.bfloat16, device=dev),
                      dw_up=torch.empty((E, F, H), dtype=torch.bfloat16, device=dev),
                      dw_down=torch.empty((E, H, F), dtype=torch.bfloat16, device=dev))
-    check(_lib.load().moe_layer_backward(
+    lib, st = _lib.load(), _stream(dev)
+    if split:
+        check(lib.moe_layer_backward_data(
+            _p(x), MOE_BF16, _p(w_router), _p(w_gate), _p(w_up), _p(w_down), MOE_BF16, T, H, F,
+            E, k, _p(dout), _p(reserve), reserve.numel(), _p(grads["dx"]),
+            _p(grads["dw_router"]), _p(workspace), workspace.numel(), st))
+        check(lib.moe_layer_backward_weights(
+            T, H, F, E, k, _p(reserve), reserve.numel(), _p(grads["dw_gate"]), _p(grads["dw_up"]),
+            _p(grads["dw_down"]), _p(workspace), workspace.numel(), st))
+        return grads
+    check(lib.moe_layer_backward(
         _p(x), MOE_BF16, _p(w_router), _p(w_gate), _p(w_up), _p(w_down), MOE_BF16, T, H, F, E, k,
         _p(dout), _p(reserve), reserve.numel(), _p(grads["dx"]), _p(grads["dw_router"]),
         _p(grads["dw_gate"]), _p(grads["dw_up"]), _p(grads["dw_down"]), _p(workspace),
-        workspace.numel(), _stream(dev)))
+        workspace.numel(), st))
+    return grads
+
+
+def moe_layer_backward_weights(reserve: torch.Tensor, workspace: torch.Tensor, grads: dict,
+                               T: int, H: int, F: int, E: int, k: int = 2):
+    """The weight step alone (dw_gate, dw_up, dw_down into grads), reading
+    what an earlier moe_layer_backward data step left in workspace."""
+    _need(reserve, "reserve", torch.uint8, 1)
+    _need(workspace, "workspace", torch.uint8, 1)
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        _need(grads[n], n, torch.bfloat16, 3)
+    check(_lib.load().moe_layer_backward_weights(
+        T, H, F, E, k, _p(reserve), reserve.numel(), _p(grads["dw_gate"]), _p(grads["dw_up"]),
+        _p(grads["dw_down"]), _p(workspace), workspace.numel(), _stream(reserve.device)))
     return grads

@@ -633,21 +633,18 @@ moe_status moe_layer_forward_train(const void* x, moe_dtype act_dtype, const flo
                     "combine launch");
 }
 
-moe_status moe_layer_backward(const void* x, moe_dtype act_dtype, const float* w_router,
-                              const void* w_gate, const void* w_up, const void* w_down,
-                              moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
-                              int32_t k, const void* dout, const void* reserve,
-                              size_t reserve_bytes, void* dx, float* dw_router, void* dw_gate,
-                              void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
-                              moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the backward entry points. data: dout and dx are needed
+// (the data step); the weight gradients are checked by whichever step writes
+// them.
+moe_status check_backward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k, moe_dtype act,
+                          moe_dtype wt, const void* reserve, size_t reserve_bytes, const void* ws,
+                          size_t ws_bytes) {
   moe_status st;
-  if ((st = check_train(T, H, F, E, k, act_dtype, w_dtype))) return st;
-  REQUIRE(w_router && w_gate && w_up && w_down && dw_router && dw_gate && dw_up && dw_down,
-          MOE_ERR_INVALID_ARGUMENT, "weights and weight gradients must be non-NULL");
-  REQUIRE(aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) &&
-              aligned16(dw_router) && aligned16(dw_gate) && aligned16(dw_up) &&
-              aligned16(dw_down),
-          MOE_ERR_INVALID_ARGUMENT, "weights and weight gradients must be 16-byte aligned");
+  if ((st = check_train(T, H, F, E, k, act, wt))) return st;
   const TrainReserve rneed = train_reserve_layout(nullptr, T, H, F, E, k);
   REQUIRE(reserve && reserve_bytes >= rneed.total && aligned16(reserve),
           MOE_ERR_WORKSPACE_TOO_SMALL, "training reserve: need %zu bytes, got %zu", rneed.total,
@@ -656,49 +653,48 @@ moe_status moe_layer_backward(const void* x, moe_dtype act_dtype, const float* w
   REQUIRE(ws && ws_bytes >= wneed.total && aligned16(ws), MOE_ERR_WORKSPACE_TOO_SMALL,
           "backward workspace: need %zu bytes (16-byte aligned), got %zu", wneed.total,
           ws ? ws_bytes : (size_t)0);
-  if (T > 0) {
-    REQUIRE(x && dout && dx, MOE_ERR_INVALID_ARGUMENT, "x, dout and dx must be non-NULL");
-    REQUIRE(aligned16(x) && aligned16(dout) && aligned16(dx), MOE_ERR_INVALID_ARGUMENT,
-            "x, dout and dx must be 16-byte aligned");
-  }
-  hipStream_t s = (hipStream_t)stream;
-  const TrainReserve R =
-      train_reserve_layout(static_cast<char*>(const_cast<void*>(reserve)), T, H, F, E, k);
-  const BwdWs B = bwd_ws_layout(static_cast<char*>(ws), T, H, F, E, k);
-  hipError_t e = hipSuccess;
-#define MOE_STEP(call, what) \
-  do {                       \
-    e = (call);              \
-    if (e != hipSuccess) return hip_status(e, what); \
+  return ok();
+}
+
+#define MOE_STEP(call, what)                          \
+  do {                                                \
+    hipError_t e_ = (call);                           \
+    if (e_ != hipSuccess) return hip_status(e_, what); \
   } while (0)
-  // routing-weight and selected-logit gradients; dy = w * dout per kept row
+
+// combine backward, dh = dy W_down, SwiGLU backward, dx rows = [dg | du]
+// [W_gate | W_up], dx and the router gradient; leaves dy, h, [dg | du] and x
+// transposed into the padded per-expert layout for the weight step
+moe_status backward_data(const void* x, const float* w_router, const void* w_gate,
+                         const void* w_up, const void* w_down, int64_t T, int32_t H, int32_t F,
+                         int32_t E, int32_t k, const void* dout, const TrainReserve& R,
+                         void* dx, float* dw_router, const BwdWs& B, hipStream_t s) {
+  const int64_t N = T * k;
   if (T > 0)
     MOE_STEP(launch_combine_bwd(dout, R.y, R.slot_row, R.w, R.idx, T, H, E, k, B.dy, B.dw, B.dl,
                                 s), "combine backward launch");
-  // dh = dy W_down (W_down^T as the k-contiguous operand of the down-mode GEMM)
+  // W_down^T is the k-contiguous operand of the down-mode GEMM that gives dh
   MOE_STEP(launch_weight_transpose(w_down, E, H, F, B.wdT, H, 0, s), "weight transpose launch");
-  FfnArgs a1{nullptr, nullptr, R.offsets, T, F, H, E, k, nullptr, nullptr, B.wdT, nullptr, nullptr,
-             nullptr, B.dy, B.dh, nullptr, nullptr, nullptr};
-  if (T > 0) MOE_STEP(launch_down_tiled(a1, WT_BF16, s), "dh GEMM launch");
-  if (T > 0)
-    MOE_STEP(launch_swiglu_bwd(B.dh, R.g, R.u, R.offsets, E, T * k, F, B.dgu, s),
+  const FfnArgs a1{nullptr, nullptr, R.offsets, T, F, H, E, k, nullptr, nullptr, B.wdT, nullptr,
+                   nullptr, nullptr, B.dy, B.dh, nullptr, nullptr, nullptr};
+  if (T > 0) {
+    MOE_STEP(launch_down_tiled(a1, WT_BF16, s), "dh GEMM launch");
+    MOE_STEP(launch_swiglu_bwd(B.dh, R.g, R.u, R.offsets, E, N, F, B.dgu, s),
              "SwiGLU backward launch");
-  // dx rows = [dg | du] [W_gate | W_up] (one down-mode GEMM over K = 2F)
+  }
+  // one down-mode GEMM over K = 2F for the per-row input gradient
   MOE_STEP(launch_weight_transpose(w_gate, E, F, H, B.wguT, 2 * (int64_t)F, 0, s),
            "weight transpose launch");
   MOE_STEP(launch_weight_transpose(w_up, E, F, H, B.wguT, 2 * (int64_t)F, F, s),
            "weight transpose launch");
-  FfnArgs a2{nullptr, nullptr, R.offsets, T, H, 2 * F, E, k, nullptr, nullptr, B.wguT, nullptr,
-             nullptr, nullptr, B.dgu, B.dxr, nullptr, nullptr, nullptr};
+  const FfnArgs a2{nullptr, nullptr, R.offsets, T, H, 2 * F, E, k, nullptr, nullptr, B.wguT,
+                   nullptr, nullptr, nullptr, B.dgu, B.dxr, nullptr, nullptr, nullptr};
   if (T > 0) {
     MOE_STEP(launch_down_tiled(a2, WT_BF16, s), "dx GEMM launch");
     MOE_STEP(launch_dx_combine(B.dxr, R.slot_row, R.idx, B.dl, w_router, T, H, E, k, dx, s),
              "dx combine launch");
   }
   MOE_STEP(launch_router_wgrad(x, B.dl, T, H, E, B.part, dw_router, s), "router gradient launch");
-  // weight gradients: contractions over each expert's rows, as GEMMs over
-  // the transposed activations
-  const int64_t N = T * k;
   if (T > 0) {
     MOE_STEP(launch_act_transpose(B.dy, H, nullptr, k, R.offsets, E, N, H, B.dyT, B.Lp, s),
              "transpose launch");
@@ -709,15 +705,92 @@ moe_status moe_layer_backward(const void* x, moe_dtype act_dtype, const float* w
     MOE_STEP(launch_act_transpose(x, H, R.perm, k, R.offsets, E, N, H, B.xT, B.Lp, s),
              "transpose launch");
   }
-  // dW_down[e] = dy_e^T h_e: M = H, N = F; the F-row operand is the larger,
-  // so the m tiles sharing one of its blocks run together
+  return ok();
+}
+
+// the weight gradients: per-expert contractions over the expert's rows
+moe_status backward_weights(int32_t H, int32_t F, int32_t E, const TrainReserve& R,
+                            void* dw_gate, void* dw_up, void* dw_down, const BwdWs& B,
+                            hipStream_t s) {
+  // dW_down[e] = dy_e^T h_e (M = H, N = F); the F-row operand is the larger,
+  // so the m tiles that share one of its blocks run together
   const WgradArgs gd{B.dyT, B.hT, B.Lp, R.offsets, E, H, F, H, dw_down, nullptr, 1};
   MOE_STEP(launch_wgrad(gd, s), "down weight gradient launch");
-  // [dW_gate; dW_up][e] = [dg | du]_e^T x_e: M = 2F, N = H
+  // [dW_gate; dW_up][e] = [dg | du]_e^T x_e (M = 2F, N = H)
   const WgradArgs ggu{B.dguT, B.xT, B.Lp, R.offsets, E, 2 * F, H, F, dw_gate, dw_up, 0};
   MOE_STEP(launch_wgrad(ggu, s), "gate/up weight gradient launch");
-#undef MOE_STEP
   return ok();
+}
+#undef MOE_STEP
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_backward_data(const void* x, moe_dtype act_dtype, const float* w_router,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
+                                   int32_t k, const void* dout, const void* reserve,
+                                   size_t reserve_bytes, void* dx, float* dw_router, void* ws,
+                                   size_t ws_bytes, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_backward(T, H, F, E, k, act_dtype, w_dtype, reserve, reserve_bytes, ws,
+                           ws_bytes)))
+    return st;
+  REQUIRE(w_router && w_gate && w_up && w_down && dw_router, MOE_ERR_INVALID_ARGUMENT,
+          "weights and dw_router must be non-NULL");
+  REQUIRE(aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) &&
+              aligned16(dw_router),
+          MOE_ERR_INVALID_ARGUMENT, "weights and dw_router must be 16-byte aligned");
+  if (T > 0) {
+    REQUIRE(x && dout && dx, MOE_ERR_INVALID_ARGUMENT, "x, dout and dx must be non-NULL");
+    REQUIRE(aligned16(x) && aligned16(dout) && aligned16(dx), MOE_ERR_INVALID_ARGUMENT,
+            "x, dout and dx must be 16-byte aligned");
+  }
+  const TrainReserve R =
+      train_reserve_layout(static_cast<char*>(const_cast<void*>(reserve)), T, H, F, E, k);
+  const BwdWs B = bwd_ws_layout(static_cast<char*>(ws), T, H, F, E, k);
+  return backward_data(x, w_router, w_gate, w_up, w_down, T, H, F, E, k, dout, R, dx, dw_router,
+                       B, (hipStream_t)stream);
+}
+
+moe_status moe_layer_backward_weights(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                                      const void* reserve, size_t reserve_bytes, void* dw_gate,
+                                      void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_backward(T, H, F, E, k, MOE_BF16, MOE_BF16, reserve, reserve_bytes, ws,
+                           ws_bytes)))
+    return st;
+  REQUIRE(dw_gate && dw_up && dw_down, MOE_ERR_INVALID_ARGUMENT,
+          "dw_gate, dw_up and dw_down must be non-NULL");
+  REQUIRE(aligned16(dw_gate) && aligned16(dw_up) && aligned16(dw_down), MOE_ERR_INVALID_ARGUMENT,
+          "dw_gate, dw_up and dw_down must be 16-byte aligned");
+  const TrainReserve R =
+      train_reserve_layout(static_cast<char*>(const_cast<void*>(reserve)), T, H, F, E, k);
+  const BwdWs B = bwd_ws_layout(static_cast<char*>(ws), T, H, F, E, k);
+  return backward_weights(H, F, E, R, dw_gate, dw_up, dw_down, B, (hipStream_t)stream);
+}
+
+moe_status moe_layer_backward(const void* x, moe_dtype act_dtype, const float* w_router,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              moe_dtype w_dtype, int64_t T, int32_t H, int32_t F, int32_t E,
+                              int32_t k, const void* dout, const void* reserve,
+                              size_t reserve_bytes, void* dx, float* dw_router, void* dw_gate,
+                              void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                              moe_stream_t stream) {
+  moe_status st;
+  // the weight step's own checks first, so that a failure enqueues nothing
+  REQUIRE(dw_gate && dw_up && dw_down, MOE_ERR_INVALID_ARGUMENT,
+          "dw_gate, dw_up and dw_down must be non-NULL");
+  REQUIRE(aligned16(dw_gate) && aligned16(dw_up) && aligned16(dw_down), MOE_ERR_INVALID_ARGUMENT,
+          "dw_gate, dw_up and dw_down must be 16-byte aligned");
+  if ((st = moe_layer_backward_data(x, act_dtype, w_router, w_gate, w_up, w_down, w_dtype, T, H,
+                                    F, E, k, dout, reserve, reserve_bytes, dx, dw_router, ws,
+                                    ws_bytes, stream)))
+    return st;
+  return moe_layer_backward_weights(T, H, F, E, k, reserve, reserve_bytes, dw_gate, dw_up,
+                                    dw_down, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -247,3 +247,27 @@ def test_training_sizes(lib):
     assert 3 * E * H * F * 2 + rows <= w < 3 * E * H * F * 2 + rows + 64 * 2 ** 20
     assert lib.moe_layer_train_reserve_bytes(0, H, F, E, k) > 0
     assert lib.moe_layer_backward_workspace_bytes(-1, H, F, E, k) == 0
+
+
+def test_backward_step_argument_errors(lib):
+    T, H, F, E, k = 32, 128, 256, 8, 2
+    nres = lib.moe_layer_train_reserve_bytes(T, H, F, E, k)
+    nws = lib.moe_layer_backward_workspace_bytes(T, H, F, E, k)
+    data = lambda **kw: lib.moe_layer_backward_data(
+        P, kw.get("act", BF16), P, P, P, P, BF16, T, H, F, E, k, kw.get("dout", P), P, nres,
+        kw.get("dx", P), kw.get("dwr", P), kw.get("ws", P), kw.get("nws", nws), None)
+    wts = lambda **kw: lib.moe_layer_backward_weights(
+        kw.get("T", T), H, F, E, k, P, kw.get("nres", nres), kw.get("dwg", P), P, P,
+        kw.get("ws", P), nws, None)
+    assert data(dx=None) == INV
+    assert data(dwr=MIS) == INV
+    assert data(act=F32) == UNS
+    assert data(nws=nws - 1) == WS
+    assert wts(dwg=None) == INV
+    assert wts(dwg=MIS) == INV
+    assert wts(ws=None) == WS
+    assert wts(nres=16) == WS
+    assert wts(T=-1) == INV
+    # the fused call checks the weight step's pointers before enqueuing anything
+    assert lib.moe_layer_backward(P, BF16, P, P, P, P, BF16, T, H, F, E, k, P, P, nres, P, P, MIS,
+                                  P, P, P, nws, None) == INV

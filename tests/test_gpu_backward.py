@@ -116,6 +116,19 @@ def test_backward_is_deterministic(moe):
                            g2[n].view(torch.int16) if g2[n].dtype == torch.bfloat16 else g2[n]), n
 
 
+def test_split_backward_equals_fused(moe):
+    cfg = synth.get_config("p_cap")
+    d = to_device(synth.generate_host(cfg))
+    dout = dev_tensor(synth.grad_output(cfg.T, cfg.H, seed=6), "bf16")
+    _, res, g1 = _run(moe, d, dout, cfg)
+    g2 = moe.moe_layer_backward(d["x"], d["wr"], d["wg"], d["wu"], d["wd"], dout, res, k=2,
+                                split=True)
+    torch.cuda.synchronize()
+    for n in g1:
+        assert torch.equal(g1[n].view(torch.int16) if g1[n].dtype == torch.bfloat16 else g1[n],
+                           g2[n].view(torch.int16) if g2[n].dtype == torch.bfloat16 else g2[n]), n
+
+
 def test_backward_empty_batch(moe):
     cfg = synth.get_config("p_bf16").with_(T=0)
     d = to_device(synth.generate_host(cfg))
