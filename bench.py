@@ -56,6 +56,9 @@ KERNEL_SOURCES = {
     "gateup_tiled": ["sparse_moe_transformer_top_amd/csrc/ffn_tiled.hip",
                      "sparse_moe_transformer_top_amd/csrc/common.h",
                      "sparse_moe_transformer_top_amd/csrc/grouped.h"],
+    "wgrad": ["sparse_moe_transformer_top_amd/csrc/ffn_tiled.hip",
+              "sparse_moe_transformer_top_amd/csrc/common.h",
+              "sparse_moe_transformer_top_amd/csrc/grouped.h"],
 }
 
 
@@ -491,7 +494,7 @@ def main():
                          "achieved": round(wach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(wach / BF16_PEAK_TFLOPS, 4),
                          "algorithmic_flops": wflops / 2, "mean_ms": round(wt / 2, 4),
-                         "traffic": None}}
+                         "traffic": traffic_from_profiles("wgrad", "train")}}
         del tr
         torch.cuda.empty_cache()
 

@@ -678,7 +678,7 @@ moe_status backward_data(const void* x, const float* w_router, const void* w_gat
   const FfnArgs a1{nullptr, nullptr, R.offsets, T, F, H, E, k, nullptr, nullptr, B.wdT, nullptr,
                    nullptr, nullptr, B.dy, B.dh, nullptr, nullptr, nullptr};
   if (T > 0) {
-    MOE_STEP(launch_down_tiled(a1, WT_BF16, s), "dh GEMM launch");
+    MOE_STEP(launch_dgrad_tiled(a1, s), "dh GEMM launch");
     MOE_STEP(launch_swiglu_bwd(B.dh, R.g, R.u, R.offsets, E, N, F, B.dgu, s),
              "SwiGLU backward launch");
   }
@@ -690,7 +690,7 @@ moe_status backward_data(const void* x, const float* w_router, const void* w_gat
   const FfnArgs a2{nullptr, nullptr, R.offsets, T, H, 2 * F, E, k, nullptr, nullptr, B.wguT,
                    nullptr, nullptr, nullptr, B.dgu, B.dxr, nullptr, nullptr, nullptr};
   if (T > 0) {
-    MOE_STEP(launch_down_tiled(a2, WT_BF16, s), "dx GEMM launch");
+    MOE_STEP(launch_dgrad_tiled(a2, s), "dx GEMM launch");
     MOE_STEP(launch_dx_combine(B.dxr, R.slot_row, R.idx, B.dl, w_router, T, H, E, k, dx, s),
              "dx combine launch");
   }

@@ -66,6 +66,9 @@ hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
 // bf16 gate/up that also writes g_save and u_save (training forward)
 hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s);
+// bf16 down-mode product y = h wd^T for the backward (dh and the dx rows,
+// with H, F, h, wd, y standing for the product's N, K, A, B and output)
+hipError_t launch_dgrad_tiled(const FfnArgs& a, hipStream_t s);
 
 // Backward weight-gradient GEMM (ffn_tiled.hip), bf16: per expert e,
 // C_e[m][n] = sum over the expert's padded k range of a[m][k] * b[n][k].
