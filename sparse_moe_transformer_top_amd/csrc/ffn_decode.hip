@@ -59,10 +59,10 @@ template <int WT, int NB> struct InFlight { static constexpr int N = 4; };
 template <> struct InFlight<WT_BF16, 1> { static constexpr int N = 8; };
 // int4 needs 64 bytes of activations per 16 bytes of weights per lane
 #ifndef MOE_I4_GU_INF
-#define MOE_I4_GU_INF 2
+#define MOE_I4_GU_INF 1
 #endif
 #ifndef MOE_I4_DN_INF
-#define MOE_I4_DN_INF 4
+#define MOE_I4_DN_INF 2
 #endif
 template <> struct InFlight<WT_I4, 2> { static constexpr int N = MOE_I4_GU_INF; };
 template <> struct InFlight<WT_I4, 1> { static constexpr int N = MOE_I4_DN_INF; };
@@ -132,11 +132,10 @@ MOE_DEV void stream_steps(const uint16_t* arow, const char* const (&wrow)[NB], i
 // four MFMAs take the codes as bf16 128 + u; four more with a constant -136
 // operand remove the bias (u - 8 is the value), and the step's sum is scaled
 // by the row's group scale into the running sums.
-template <int NB, int W>
+template <int NB, int W, int kInFlight>
 MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB],
                              const float* const (&srow)[NB], int s_begin, int s_end, int wave,
                              int g, f32x4 (&acc)[NB]) {
-  constexpr int kInFlight = InFlight<WT_I4, NB>::N;
   constexpr uint32_t kNeg136 = 0xC308C308u;   // two bf16 -136.0
   const u32x4 cneg = {kNeg136, kNeg136, kNeg136, kNeg136};
   const u32x4 z = {0u, 0u, 0u, 0u};
@@ -207,13 +206,7 @@ __global__ __launch_bounds__(GateUpWaves<WT>::N * 64) void gateup_decode_kernel(
   f32x4 acc[2];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   acc[1] = acc[0];
-  if (WT == WT_I4) {
-    const int64_t row = (int64_t)e * a.F + n;
-    const char* const wrow[2] = {static_cast<const char*>(a.wg) + row * (a.H / 2),
-                                 static_cast<const char*>(a.wu) + row * (a.H / 2)};
-    const float* const srow[2] = {a.sg + row * (a.H / 128), a.su + row * (a.H / 128)};
-    stream_steps_i4<2, kWaves>(arow, wrow, srow, 0, a.H / Step<WT>::K, wave, g, acc);
-  } else {
+  {
     const int64_t roff = ((int64_t)e * a.F + n) * a.H * Step<WT>::ESZ;
     const char* const wrow[2] = {static_cast<const char*>(a.wg) + roff,
                                  static_cast<const char*>(a.wu) + roff};
@@ -272,12 +265,7 @@ __global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnA
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   int kb, ke;
   split_range(a.F / Step<WT>::K, kSplit, split, kb, ke);
-  if (WT == WT_I4) {
-    const int64_t row = (int64_t)e * a.H + n;
-    const char* const wrow[1] = {static_cast<const char*>(a.wd) + row * (a.F / 2)};
-    const float* const srow[1] = {a.sd + row * (a.F / 128)};
-    stream_steps_i4<1, kWaves>(arow, wrow, srow, kb, ke, wave, g, acc);
-  } else {
+  {
     const char* const wrow[1] = {static_cast<const char*>(a.wd) +
                                  ((int64_t)e * a.H + n) * a.F * Step<WT>::ESZ};
     stream_steps<WT, 1, kWaves>(arow, wrow, kb, ke, wave, g, acc);
@@ -298,6 +286,129 @@ __global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnA
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) ys += red[w][v][lane];
     if (WT == WT_I8) ys *= a.sd[(int64_t)e * a.H + col];
+    part[(int64_t)(r0 + row) * a.H + col] = ys;
+  }
+}
+
+// int4 weights: a work-group covers NT tiles of 16 output columns. A lane's
+// activation chunks (64 bytes for the 32 codes of each 16-byte weight load)
+// then serve the weight rows of all NT tiles, which cuts the activation
+// requests per weight byte by NT (with int4 codes the activations, 2 bytes
+// per code against half a byte of weight, were two thirds of the bytes a
+// work-group requested). Measured at the Grok-1 decode shape (T = 8): two
+// tiles with one step in flight per lane for gate/up (0.427 ms against 0.441
+// for one tile with two steps; four tiles, or two with two steps, cost
+// occupancy and were slower), two tiles with two steps for down (0.224 ms
+// against 0.266 for one tile with four).
+#ifndef MOE_I4_GU_NT
+#define MOE_I4_GU_NT 2
+#endif
+#ifndef MOE_I4_DN_NT
+#define MOE_I4_DN_NT 2
+#endif
+constexpr int kI4GateUpTiles = MOE_I4_GU_NT;
+constexpr int kI4DownTiles = MOE_I4_DN_NT;
+
+template <int NT>
+__global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64) void gateup_decode_i4_kernel(FfnArgs a) {
+  constexpr int kWaves = GateUpWaves<WT_I4>::N;
+  static_assert(NT <= kWaves, "one wave per tile in the epilogue");
+  __shared__ float red[kWaves][2 * NT][4][64];
+  const int groups = (a.F + 16 * NT - 1) / (16 * NT);
+  const int e = blockIdx.x / groups;
+  const int n0 = (blockIdx.x % groups) * 16 * NT;
+  const int r0 = a.offsets[e];
+  const int ne = a.offsets[e + 1] - r0;
+  if (ne <= 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const uint16_t* arow = nullptr;
+  if (i < ne) arow = static_cast<const uint16_t*>(a.x) + (int64_t)(a.perm[r0 + i] / a.k) * a.H;
+  const char* wrow[2 * NT];
+  const float* srow[2 * NT];
+  f32x4 acc[2 * NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t row = (int64_t)e * a.F + min(n0 + 16 * t + i, a.F - 1);
+    wrow[2 * t] = static_cast<const char*>(a.wg) + row * (a.H / 2);
+    wrow[2 * t + 1] = static_cast<const char*>(a.wu) + row * (a.H / 2);
+    srow[2 * t] = a.sg + row * (a.H / 128);
+    srow[2 * t + 1] = a.su + row * (a.H / 128);
+    acc[2 * t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[2 * t + 1] = acc[2 * t];
+  }
+  stream_steps_i4<2 * NT, kWaves, InFlight<WT_I4, 2>::N>(arow, wrow, srow, 0, a.H / 128, wave, g,
+                                                         acc);
+#pragma unroll
+  for (int b = 0; b < 2 * NT; ++b)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][b][v][lane] = acc[b][v];
+  __syncthreads();
+  // wave t writes tile t (t < NT), summing the waves' partials in wave order
+  if (wave >= NT) return;
+  const int col = n0 + 16 * wave + i;
+  if (col >= a.F) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int row = 4 * g + v;
+    if (row >= ne) continue;
+    float gs = 0.f, us = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      gs += red[w][2 * wave][v][lane];
+      us += red[w][2 * wave + 1][v][lane];
+    }
+    static_cast<uint16_t*>(a.h)[(int64_t)(r0 + row) * a.F + col] = f32_to_bf16_bits(swiglu(gs, us));
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(DownWaves<WT_I4>::N * 64) void down_decode_i4_kernel(FfnArgs a) {
+  constexpr int kWaves = DownWaves<WT_I4>::N;
+  constexpr int kSplit = DownSplit<WT_I4>::N;
+  static_assert(NT <= kWaves, "one wave per tile in the epilogue");
+  __shared__ float red[kWaves][NT][4][64];
+  const int groups = (a.H + 16 * NT - 1) / (16 * NT);
+  const int split = blockIdx.x % kSplit;
+  const int tile = blockIdx.x / kSplit;
+  const int e = tile / groups;
+  const int n0 = (tile % groups) * 16 * NT;
+  const int r0 = a.offsets[e];
+  const int ne = a.offsets[e + 1] - r0;
+  if (ne <= 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const uint16_t* arow = i < ne ? static_cast<const uint16_t*>(a.h) + (int64_t)(r0 + i) * a.F
+                                : nullptr;
+  const char* wrow[NT];
+  const float* srow[NT];
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t row = (int64_t)e * a.H + min(n0 + 16 * t + i, a.H - 1);
+    wrow[t] = static_cast<const char*>(a.wd) + row * (a.F / 2);
+    srow[t] = a.sd + row * (a.F / 128);
+    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  int kb, ke;
+  split_range(a.F / 128, kSplit, split, kb, ke);
+  stream_steps_i4<NT, kWaves, InFlight<WT_I4, 1>::N>(arow, wrow, srow, kb, ke, wave, g, acc);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][t][v][lane] = acc[t][v];
+  __syncthreads();
+  if (wave >= NT) return;
+  const int col = n0 + 16 * wave + i;
+  if (col >= a.H) return;
+  float* part = static_cast<float*>(a.ws) + (int64_t)split * a.T * a.k * a.H;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int row = 4 * g + v;
+    if (row >= ne) continue;
+    float ys = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) ys += red[w][wave][v][lane];
     part[(int64_t)(r0 + row) * a.H + col] = ys;
   }
 }
@@ -338,8 +449,10 @@ hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
     hipLaunchKernelGGL(gateup_decode_kernel<WT_I8>, grid, dim3(GateUpWaves<WT_I8>::N * 64), 0, s,
                        a);
   else if (wt == WT_I4)
-    hipLaunchKernelGGL(gateup_decode_kernel<WT_I4>, grid, dim3(GateUpWaves<WT_I4>::N * 64), 0, s,
-                       a);
+    hipLaunchKernelGGL(gateup_decode_i4_kernel<kI4GateUpTiles>,
+                       dim3((unsigned)(a.E * ((a.F + 16 * kI4GateUpTiles - 1) /
+                                              (16 * kI4GateUpTiles)))),
+                       dim3(GateUpWaves<WT_I4>::N * 64), 0, s, a);
   else
     hipLaunchKernelGGL(gateup_decode_kernel<WT_BF16>, grid, dim3(GateUpWaves<WT_BF16>::N * 64), 0,
                        s, a);
@@ -356,7 +469,9 @@ hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
                        dim3(DownWaves<WT_I8>::N * 64), 0, s, a);
     nsplit = DownSplit<WT_I8>::N;
   } else if (wt == WT_I4) {
-    hipLaunchKernelGGL(down_decode_kernel<WT_I4>, grid(DownSplit<WT_I4>::N),
+    const unsigned groups = (unsigned)((a.H + 16 * kI4DownTiles - 1) / (16 * kI4DownTiles));
+    hipLaunchKernelGGL(down_decode_i4_kernel<kI4DownTiles>,
+                       dim3((unsigned)a.E * groups * DownSplit<WT_I4>::N),
                        dim3(DownWaves<WT_I4>::N * 64), 0, s, a);
     nsplit = DownSplit<WT_I4>::N;
   } else {
