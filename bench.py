@@ -489,7 +489,7 @@ def main():
             "mfma_frac": round(tflops / (tms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "stages_ms": {"forward_train": round(fw, 3), "backward": round(bw, 3),
                           "backward_weights": round(wt, 3)},
-            "roofline": {"bound": "mfma", "kernel": "wgrad_mfma_kernel (dW_down, then "
+            "roofline": {"bound": "mfma", "kernel": "wgrad_tn_kernel (dW_down, then "
                          "dW_gate|dW_up: 2 launches per step)",
                          "achieved": round(wach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(wach / BF16_PEAK_TFLOPS, 4),

@@ -329,8 +329,9 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
  *   int32, dropped [T*k] uint8 (all as moe_dispatch / moe_router_topk
  *   define them), dispatch scratch (moe_dispatch_workspace_bytes), then the
  *   bf16 pre-activations g [T*k,F] and u [T*k,F] (each rounded once from the
- *   float32 accumulator), h [T*k,F] and y_perm [T*k,H] (as moe_expert_ffn
- *   defines them). Rows at or past offsets[E] are unwritten.
+ *   float32 accumulator), h [T*k+64,F] and y_perm [T*k,H] (as
+ *   moe_expert_ffn defines them; h has 64 rows of slack that the backward
+ *   reads and masks out). Rows at or past offsets[E] are unwritten.
  * moe_layer_backward: given dout [T,H] bf16 (the gradient of out) and the
  *   reserve of the forward on the same x and weights, writes
  *   dx [T,H] bf16, dw_router [E,H] float32, dw_gate [E,F,H], dw_up [E,F,H]
@@ -338,15 +339,17 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
  *   that received no rows). Float32 accumulation throughout; bf16 rounding
  *   of the intermediates dy, dh, [dg | du] and the per-row dx, and once of
  *   each output. ws: device scratch of moe_layer_backward_workspace_bytes
- *   (...) bytes, 16-byte aligned (it holds the transposed weights, about
- *   3*E*H*F*2 bytes, and the row gradients). The reserve is only read.
+ *   (...) bytes, 16-byte aligned (it holds the row gradients dy, dh,
+ *   [dg | du] and the per-row dx, and the x rows in dispatch order: about
+ *   T*k*(3H + 3F)*2 bytes; the weights are used as stored, no transposed
+ *   copies). The reserve is only read.
  * moe_layer_backward is exactly moe_layer_backward_data followed by
  *   moe_layer_backward_weights on one stream with the same reserve and ws:
  *   the data step writes dx and dw_router and leaves in ws what the weight
  *   step reads (so a schedule may run the weight step later, as long as ws
  *   and the reserve are left untouched in between); the weight step writes
- *   dw_gate, dw_up and dw_down and reads only ws and the reserve's dispatch
- *   offsets (neither x nor the weights).
+ *   dw_gate, dw_up and dw_down and reads only ws and the reserve (h and the
+ *   dispatch offsets), neither x nor the weights.
  * ------------------------------------------------------------------------ */
 size_t moe_layer_train_reserve_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k);
 size_t moe_layer_backward_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k);

@@ -252,7 +252,8 @@ def _align256(n: int) -> int:
 
 def train_reserve_views(reserve: torch.Tensor, T: int, H: int, F: int, E: int, k: int):
     """Views of the arrays moe_layer_forward_train keeps in the reserve (the
-    layout include/moe.h documents): routing, dispatch, g, u, h, y_perm."""
+    layout include/moe.h documents): routing, dispatch, g, u, h (its T*k
+    rows; 64 slack rows follow), y_perm."""
     N = T * k
     disp_ws = _lib.load().moe_dispatch_workspace_bytes(T, E, k)
     parts = [("topk_idx", torch.int32, (T, k)), ("topk_w", torch.float32, (T, k)),
@@ -260,14 +261,15 @@ def train_reserve_views(reserve: torch.Tensor, T: int, H: int, F: int, E: int, k
              ("perm", torch.int32, (N,)), ("slot_row", torch.int32, (N,)),
              ("dropped", torch.uint8, (N,)), ("dispatch_scratch", torch.uint8, (disp_ws,)),
              ("g", torch.bfloat16, (N, F)), ("u", torch.bfloat16, (N, F)),
-             ("h", torch.bfloat16, (N, F)), ("y_perm", torch.bfloat16, (N, H))]
+             ("h", torch.bfloat16, (N + 64, F)), ("y_perm", torch.bfloat16, (N, H))]
     out, off = {}, 0
     for name, dt, shape in parts:
         n = 1
         for d in shape:
             n *= d
         nbytes = n * torch.empty((), dtype=dt).element_size()
-        out[name] = reserve[off:off + nbytes].view(dt).view(shape)
+        out[name] = reserve[off:off + nbytes].view(dt).view(shape)[:N] if name == "h" else \
+            reserve[off:off + nbytes].view(dt).view(shape)
         off += _align256(nbytes)
     return out
 

@@ -1,4 +1,4 @@
-// The layer's backward: everything around the GEMMs.
+// The layer's backward: everything around the GEMMs (those are in ffn_tiled.hip).
 //
 // n4n.ai page "How does Grok-1 use a mixture-of-experts design?": the layer
 // of section "The high-level architecture" (router, top-2 softmax over the
@@ -14,95 +14,16 @@
 //                 as one row [dg | du] of 2F.
 //   dx_combine:   dx_t = sum over kept slots of dx_r + sum_j dl[t,idx_j] Wr[idx_j].
 //   router wgrad: dWr[e] = sum_t dl[t,e] x_t.
-//   transposes:   the GEMM kernels take k-contiguous operands; the backward
-//                 contracts over H for dh, over F for dx and over tokens for
-//                 the weight gradients, so the weights and the activations
-//                 are transposed once (activations into per-expert segments
-//                 padded to 64 with zeros).
 // Every reduction runs in a fixed order (no atomics): results are
 // deterministic.
 #include "common.h"
-#include "grouped.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int TB = 64;   // transpose tile (elements)
-
 MOE_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 MOE_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-
-// A 64 x 64 bf16 tile through LDS. Phase 1: 8 lanes read one source row's
-// 128 bytes (srow(i) gives row i's first element, or null for a zero row);
-// chunk cc of row i sits at chunk cc ^ (i / 8) of the LDS row, so in phase 2
-// the 8 rows 8q..8q+7 that one lane gathers for a column lie in distinct
-// banks across q. Phase 2: 8 lanes write one destination row's 128 bytes
-// (the tile's column c, positions 8q..8q+7).
-template <typename SrcRow, typename DstRow>
-MOE_DEV void transpose_tile(SrcRow srow, DstRow drow) {
-  __shared__ __align__(16) uint16_t tile[TB][TB];
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int i = it * 32 + t / 8, cc = t % 8;
-    const uint16_t* src = srow(i);
-    const u32x4 v = src ? ld16(src + cc * 8) : u32x4{0u, 0u, 0u, 0u};
-    st16(&tile[i][(cc ^ (i >> 3)) * 8], v);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int c = it * 32 + t / 8, q = t % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int z = 0; z < 8; z += 2) {
-      const uint32_t lo = tile[8 * q + z][((c >> 3) ^ q) * 8 + (c & 7)];
-      const uint32_t hi = tile[8 * q + z + 1][((c >> 3) ^ q) * 8 + (c & 7)];
-      w[z / 2] = lo | (hi << 16);
-    }
-    st16(drow(c) + 8 * q, u32x4{w[0], w[1], w[2], w[3]});
-  }
-}
-
-// dst[e][c][col0 + r] = src[e][r][c] for a batch of [R][C] matrices.
-__global__ __launch_bounds__(256) void weight_transpose_kernel(const uint16_t* __restrict__ src,
-                                                               int R, int C,
-                                                               uint16_t* __restrict__ dst,
-                                                               int64_t ldd, int col0) {
-  const int c0 = blockIdx.x * TB, r0 = blockIdx.y * TB;
-  const int64_t e = blockIdx.z;
-  const uint16_t* s = src + e * R * C;
-  uint16_t* d = dst + e * C * ldd + col0;
-  transpose_tile([&](int i) { return s + (int64_t)(r0 + i) * C + c0; },
-                 [&](int c) { return d + (int64_t)(c0 + c) * ldd + r0; });
-}
-
-// dst[c][p] for positions p of the padded layout: position p_e + i of expert
-// e holds dispatch row offsets[e] + i (i < n_e), zeros up to the next
-// multiple of 64. Source row of dispatch row r: src + r * lds, or with
-// GATHER the token row src + (perm[r] / k) * lds.
-template <bool GATHER>
-__global__ __launch_bounds__(256) void act_transpose_kernel(
-    const uint16_t* __restrict__ src, int64_t lds, const int32_t* __restrict__ perm, int k,
-    const int32_t* __restrict__ offsets, int E, uint16_t* __restrict__ dst, int64_t ldd) {
-  const int p0 = blockIdx.x * TB, c0 = blockIdx.y * TB;
-  // the expert whose padded segment holds p0 (segments are multiples of 64)
-  int e = 0;
-  for (; e < E; ++e)
-    if (p0 < padded_start(offsets, e + 1, TB)) break;
-  if (e == E) return;
-  const int pe = padded_start(offsets, e, TB);
-  const int r0 = offsets[e] + (p0 - pe), r_end = offsets[e + 1];
-  transpose_tile(
-      [&](int i) -> const uint16_t* {
-        const int r = r0 + i;
-        if (r >= r_end) return nullptr;
-        const int64_t row = GATHER ? (int64_t)(perm[r] / k) : (int64_t)r;
-        return src + row * lds + c0;
-      },
-      [&](int c) { return dst + (int64_t)(c0 + c) * ldd + p0; });
-}
 
 // One wave per token: dw, dy and the selected-logit gradient.
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
@@ -306,34 +227,9 @@ unsigned stride_grid(int64_t items) {
 
 }  // namespace
 
-int64_t bwd_padded_rows(int64_t n_rows, int E) { return (n_rows + 63 * (int64_t)E + 63) / 64 * 64; }
-
 int64_t router_wgrad_chunks(int64_t T) {
   const int64_t c = router_chunk_len(T);
   return (T + c - 1) / c;
-}
-
-hipError_t launch_weight_transpose(const void* src, int E, int R, int C, void* dst, int64_t ldd,
-                                   int col0, hipStream_t s) {
-  hipLaunchKernelGGL(weight_transpose_kernel, dim3((unsigned)(C / TB), (unsigned)(R / TB), (unsigned)E),
-                     dim3(256), 0, s, static_cast<const uint16_t*>(src), R, C,
-                     static_cast<uint16_t*>(dst), ldd, col0);
-  return hipGetLastError();
-}
-
-hipError_t launch_act_transpose(const void* src, int64_t lds, const int32_t* perm, int k,
-                                const int32_t* offsets, int E, int64_t n_rows, int C, void* dst,
-                                int64_t ldd, hipStream_t s) {
-  const dim3 grid((unsigned)(bwd_padded_rows(n_rows, E) / TB), (unsigned)(C / TB));
-  if (perm)
-    hipLaunchKernelGGL(act_transpose_kernel<true>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(src), lds, perm, k, offsets, E,
-                       static_cast<uint16_t*>(dst), ldd);
-  else
-    hipLaunchKernelGGL(act_transpose_kernel<false>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(src), lds, perm, k, offsets, E,
-                       static_cast<uint16_t*>(dst), ldd);
-  return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* slot_row,

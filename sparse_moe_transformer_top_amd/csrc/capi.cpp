@@ -141,6 +141,12 @@ LayerWs layer_ws_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E, 
   return L;
 }
 
+// The weight-gradient kernel reads up to 63 rows past an expert's last
+// dispatch row (and masks them out), so the buffers it reads (h in the
+// reserve; dy, [dg | du] and the gathered x in the backward scratch) keep
+// kBwdSlackRows rows after row T*k.
+constexpr int64_t kBwdSlackRows = 64;
+
 // The training reserve (written by moe_layer_forward_train, read by
 // moe_layer_backward); the order is part of the ABI (include/moe.h).
 struct TrainReserve {
@@ -185,52 +191,40 @@ TrainReserve train_reserve_layout(char* base, int64_t T, int32_t H, int32_t F, i
   R.dws = c.take(dispatch_ws_bytes(T, E));
   R.g = c.take((size_t)N * F * 2);
   R.u = c.take((size_t)N * F * 2);
-  R.h = c.take((size_t)N * F * 2);
+  R.h = c.take((size_t)(N + kBwdSlackRows) * F * 2);
   R.y = c.take((size_t)N * H * 2);
   R.total = c.off;
   return R;
 }
 
-// Backward scratch: transposed weights, row-layout gradients, their
-// transposes in the padded per-expert layout, and the small float32 arrays.
+// Backward scratch: the row-layout gradients and the gathered x rows.
 struct BwdWs {
-  void* wdT;    // [E][F][H]
-  void* wguT;   // [E][H][2F]: W_gate^T then W_up^T
-  void* dy;     // [N][H]
+  void* dy;     // [N + slack][H]
   void* dh;     // [N][F]
-  void* dgu;    // [N][2F]: dg then du
+  void* dgu;    // [N + slack][2F]: dg then du
   void* dxr;    // [N][H]
-  void* dyT;    // [H][Lp]
-  void* xT;     // [H][Lp]
-  void* hT;     // [F][Lp]
-  void* dguT;   // [2F][Lp]
+  void* xg;     // [N + slack][H]: x rows in dispatch order
   float* dw;    // [N]
   float* dl;    // [T][E]
   float* part;  // router gradient partials
-  int64_t Lp;
+  int32_t* cnt; // [1] rows per rank of the gather (one rank)
   size_t total;
 };
 
 BwdWs bwd_ws_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E, int32_t k) {
   BwdWs B{};
-  const int64_t N = T * k;
-  const int64_t Lp = bwd_padded_rows(N, E);
-  const size_t e = (size_t)E, h = (size_t)H, f = (size_t)F;
+  const int64_t N = T * k, Ns = N + kBwdSlackRows;
+  const size_t h = (size_t)H, f = (size_t)F;
   Carver c{base, 0};
-  B.wdT = c.take(e * f * h * 2);
-  B.wguT = c.take(e * h * 2 * f * 2);
-  B.dy = c.take((size_t)N * h * 2);
+  B.dy = c.take((size_t)Ns * h * 2);
   B.dh = c.take((size_t)N * f * 2);
-  B.dgu = c.take((size_t)N * 2 * f * 2);
+  B.dgu = c.take((size_t)Ns * 2 * f * 2);
   B.dxr = c.take((size_t)N * h * 2);
-  B.dyT = c.take(h * (size_t)Lp * 2);
-  B.xT = c.take(h * (size_t)Lp * 2);
-  B.hT = c.take(f * (size_t)Lp * 2);
-  B.dguT = c.take(2 * f * (size_t)Lp * 2);
+  B.xg = c.take((size_t)Ns * h * 2);
   B.dw = static_cast<float*>(c.take((size_t)N * 4));
-  B.dl = static_cast<float*>(c.take((size_t)T * e * 4));
-  B.part = static_cast<float*>(c.take((size_t)router_wgrad_chunks(T) * e * h * 4));
-  B.Lp = Lp;
+  B.dl = static_cast<float*>(c.take((size_t)T * E * 4));
+  B.part = static_cast<float*>(c.take((size_t)router_wgrad_chunks(T) * E * h * 4));
+  B.cnt = static_cast<int32_t*>(c.take(4));
   B.total = c.off;
   return B;
 }
@@ -662,49 +656,29 @@ moe_status check_backward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
     if (e_ != hipSuccess) return hip_status(e_, what); \
   } while (0)
 
-// combine backward, dh = dy W_down, SwiGLU backward, dx rows = [dg | du]
-// [W_gate | W_up], dx and the router gradient; leaves dy, h, [dg | du] and x
-// transposed into the padded per-expert layout for the weight step
+// combine backward, dh = dy W_down, SwiGLU backward, dx rows = dg W_gate +
+// du W_up, dx and the router gradient, all on the weights as stored; then the
+// x rows in dispatch order for the weight step
 moe_status backward_data(const void* x, const float* w_router, const void* w_gate,
                          const void* w_up, const void* w_down, int64_t T, int32_t H, int32_t F,
                          int32_t E, int32_t k, const void* dout, const TrainReserve& R,
                          void* dx, float* dw_router, const BwdWs& B, hipStream_t s) {
   const int64_t N = T * k;
-  if (T > 0)
+  if (T > 0) {
     MOE_STEP(launch_combine_bwd(dout, R.y, R.slot_row, R.w, R.idx, T, H, E, k, B.dy, B.dw, B.dl,
                                 s), "combine backward launch");
-  // W_down^T is the k-contiguous operand of the down-mode GEMM that gives dh
-  MOE_STEP(launch_weight_transpose(w_down, E, H, F, B.wdT, H, 0, s), "weight transpose launch");
-  const FfnArgs a1{nullptr, nullptr, R.offsets, T, F, H, E, k, nullptr, nullptr, B.wdT, nullptr,
-                   nullptr, nullptr, B.dy, B.dh, nullptr, nullptr, nullptr};
-  if (T > 0) {
-    MOE_STEP(launch_dgrad_tiled(a1, s), "dh GEMM launch");
+    const DgradArgs dh{B.dy, R.offsets, T, E, k, F, H, H, w_down, nullptr, B.dh};
+    MOE_STEP(launch_dgrad_nn(dh, s), "dh GEMM launch");
     MOE_STEP(launch_swiglu_bwd(B.dh, R.g, R.u, R.offsets, E, N, F, B.dgu, s),
              "SwiGLU backward launch");
-  }
-  // one down-mode GEMM over K = 2F for the per-row input gradient
-  MOE_STEP(launch_weight_transpose(w_gate, E, F, H, B.wguT, 2 * (int64_t)F, 0, s),
-           "weight transpose launch");
-  MOE_STEP(launch_weight_transpose(w_up, E, F, H, B.wguT, 2 * (int64_t)F, F, s),
-           "weight transpose launch");
-  const FfnArgs a2{nullptr, nullptr, R.offsets, T, H, 2 * F, E, k, nullptr, nullptr, B.wguT,
-                   nullptr, nullptr, nullptr, B.dgu, B.dxr, nullptr, nullptr, nullptr};
-  if (T > 0) {
-    MOE_STEP(launch_dgrad_tiled(a2, s), "dx GEMM launch");
+    const DgradArgs dxr{B.dgu, R.offsets, T, E, k, H, 2 * F, F, w_gate, w_up, B.dxr};
+    MOE_STEP(launch_dgrad_nn(dxr, s), "dx GEMM launch");
     MOE_STEP(launch_dx_combine(B.dxr, R.slot_row, R.idx, B.dl, w_router, T, H, E, k, dx, s),
              "dx combine launch");
+    MOE_STEP(launch_ep_pack(x, (int64_t)H * 2, R.perm, R.offsets, N, E, k, 1, B.xg, B.cnt, s),
+             "x gather launch");
   }
   MOE_STEP(launch_router_wgrad(x, B.dl, T, H, E, B.part, dw_router, s), "router gradient launch");
-  if (T > 0) {
-    MOE_STEP(launch_act_transpose(B.dy, H, nullptr, k, R.offsets, E, N, H, B.dyT, B.Lp, s),
-             "transpose launch");
-    MOE_STEP(launch_act_transpose(R.h, F, nullptr, k, R.offsets, E, N, F, B.hT, B.Lp, s),
-             "transpose launch");
-    MOE_STEP(launch_act_transpose(B.dgu, 2 * (int64_t)F, nullptr, k, R.offsets, E, N, 2 * F,
-                                  B.dguT, B.Lp, s), "transpose launch");
-    MOE_STEP(launch_act_transpose(x, H, R.perm, k, R.offsets, E, N, H, B.xT, B.Lp, s),
-             "transpose launch");
-  }
   return ok();
 }
 
@@ -712,13 +686,14 @@ moe_status backward_data(const void* x, const float* w_router, const void* w_gat
 moe_status backward_weights(int32_t H, int32_t F, int32_t E, const TrainReserve& R,
                             void* dw_gate, void* dw_up, void* dw_down, const BwdWs& B,
                             hipStream_t s) {
-  // dW_down[e] = dy_e^T h_e (M = H, N = F); the F-row operand is the larger,
-  // so the m tiles that share one of its blocks run together
-  const WgradArgs gd{B.dyT, B.hT, B.Lp, R.offsets, E, H, F, H, dw_down, nullptr, 1};
-  MOE_STEP(launch_wgrad(gd, s), "down weight gradient launch");
+  // dW_down[e] = dy_e^T h_e (M = H, N = F); the F-column operand is the
+  // larger, so the m tiles that share one of its blocks run together
+  const WgradTnArgs gd{B.dy, H, R.h, F, R.offsets, E, H, F, H, dw_down, nullptr, 1};
+  MOE_STEP(launch_wgrad_tn(gd, s), "down weight gradient launch");
   // [dW_gate; dW_up][e] = [dg | du]_e^T x_e (M = 2F, N = H)
-  const WgradArgs ggu{B.dguT, B.xT, B.Lp, R.offsets, E, 2 * F, H, F, dw_gate, dw_up, 0};
-  MOE_STEP(launch_wgrad(ggu, s), "gate/up weight gradient launch");
+  const WgradTnArgs ggu{B.dgu, 2 * (int64_t)F, B.xg, H, R.offsets, E, 2 * F, H, F, dw_gate, dw_up,
+                        0};
+  MOE_STEP(launch_wgrad_tn(ggu, s), "gate/up weight gradient launch");
   return ok();
 }
 #undef MOE_STEP

@@ -107,29 +107,42 @@ template <int WT> struct BTile {
   static constexpr int LPW = MNB * BCH / 64 / MNW;      // B LDS-DMA loads per wave per stage
 };
 
-// The pipelined k loop, shared by ffn_mfma_kernel and wgrad_mfma_kernel as
-// macros over the kernel's own locals (a device function here changed the
-// forward kernel's instruction schedule): KT >= 1 stages of MBK through the
+// The pipelined k loop, shared by the kernels of this file as macros over
+// the kernel's own locals (a device function here changed the forward
+// kernel's instruction schedule): KT >= 1 stages of MBK through the
 // two-stage LDS ring SA/SB (sT0, sT1 hold the A tile then the B tile). This
-// wave's A loads read abase + aoff[j] (aptr[j] when WIDE), its B loads
-// bbase + boff[j]; arow / brow are the LDS tile rows whose MFMA operands the
-// wave reads; fa / fb hold two steps of operands; acc accumulates.
+// wave's A loads read MOE_AADDR(k0) + aoff[j] (aptr[j] + 2 k0 when WIDE), its
+// B loads MOE_BADDR(k0) + boff[j]; MOE_LOADA / MOE_LOADB read one 16-k step
+// of MFMA operands from a stage into fa / fb; MOE_PRE_MFMA may edit them
+// before the step's MFMAs; the scheduler is asked to place MOE_READS_AFTER(q)
+// LDS reads of the next step after the step's q-th MFMA.
+// Every kernel defines these hooks before it expands MOE_PIPELINE.
 #define MOE_ISSUE(ST, K0)                                                               \
   do {                                                                                  \
     const uint32_t la_ = ((ST) ? L1 : L0) + (uint32_t)(MLPW * wave) * 1024u;            \
     const uint32_t lb_ = ((ST) ? L1 : L0) + MBM * CH * 16 + (uint32_t)(LPWB * wave) * 1024u; \
     _Pragma("unroll") for (int j = 0; j < MLPW; ++j) {                                  \
       if (WIDE) lds_dma16(aptr[WIDE ? j : 0] + (K0) * 2, la_ + j * 1024);               \
-      else lds_dma16(abase + (K0) * 2, aoff[j], la_ + j * 1024);                        \
+      else lds_dma16(MOE_AADDR(K0), aoff[j], la_ + j * 1024);                           \
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < LPWB; ++j)                                    \
-      lds_dma16(bbase + (K0) * ESZ, boff[j], lb_ + j * 1024);                           \
+      lds_dma16(MOE_BADDR(K0), boff[j], lb_ + j * 1024);                                \
   } while (0)
-#define MOE_LOADF(SLOT, ST, KS)                                                        \
+#define MOE_LOADF(SLOT, ST, KS) \
+  do {                          \
+    MOE_LOADA(SLOT, ST, KS);    \
+    MOE_LOADB(SLOT, ST, KS);    \
+  } while (0)
+// operands of k-contiguous tiles ([row][MBK k], 16-byte chunk XOR swizzles)
+#define MOE_LOADA_ROWS(SLOT, ST, KS)                                                   \
   do {                                                                                 \
     const int chunk_ = (KS) * 2 + (lane >> 5);                                         \
     _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) fa[SLOT][mi] = as_bf16x8(        \
         SA[ST][arow[mi] * CH + (chunk_ ^ ((arow[mi] >> 1) & 7))]);                     \
+  } while (0)
+#define MOE_LOADB_ROWS(SLOT, ST, KS)                                                   \
+  do {                                                                                 \
+    const int chunk_ = (KS) * 2 + (lane >> 5);                                         \
     if (I8) {                                                                          \
       _Pragma("unroll") for (int s = 0; s < NI; ++s) {                                 \
         const uint2 q_ = reinterpret_cast<const uint2*>(                               \
@@ -140,6 +153,17 @@ template <int WT> struct BTile {
       _Pragma("unroll") for (int s = 0; s < NI; ++s) fb[SLOT][s] = as_bf16x8(          \
           SB[ST][brow[s] * BCH + (chunk_ ^ ((brow[s] >> 1) & 7))]);                    \
     }                                                                                  \
+  } while (0)
+// operands of k-major tiles ([MBK k][256 columns], see kmajor_frag)
+#define MOE_LOADA_KMAJOR(SLOT, ST, KS)                                                 \
+  do {                                                                                 \
+    _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) fa[SLOT][mi] =                   \
+        kmajor_frag(((ST) ? L1 : L0), acol[mi], (KS), lane);                           \
+  } while (0)
+#define MOE_LOADB_KMAJOR(SLOT, ST, KS)                                                 \
+  do {                                                                                 \
+    _Pragma("unroll") for (int s = 0; s < NI; ++s) fb[SLOT][s] =                       \
+        kmajor_frag(((ST) ? L1 : L0) + MBM * CH * 16, bcol[s], (KS), lane);            \
   } while (0)
 // a do-while keeps the compiler from carrying a zero-trip copy of the
 // accumulators across the loop
@@ -169,14 +193,16 @@ template <int WT> struct BTile {
               if (kt + 2 < KT) MOE_ISSUE(u, (kt + 2) * MBK);                              \
               MOE_LOADF(slot ^ 1, u ^ 1, 0);                                              \
             }                                                                             \
+            MOE_PRE_MFMA(slot, kt, ks);                                                   \
             _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                             \
               _Pragma("unroll") for (int s = 0; s < NI; ++s)                              \
                 acc[mi][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                     \
                     fa[slot][mi], fb[slot][s], acc[mi][s], 0, 0, 0);                      \
-            /* one MFMA, then one LDS read of the next step's operands */                 \
+            /* one MFMA, then MOE_READS_AFTER(q) LDS reads of the next step */            \
             _Pragma("unroll") for (int q = 0; q < MI * NI; ++q) {                         \
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          \
-              if (q < MI + NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
+              _Pragma("unroll") for (int r_ = 0; r_ < MOE_READS_AFTER(q); ++r_)           \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        \
             }                                                                             \
           }                                                                               \
         }                                                                                 \
@@ -184,6 +210,48 @@ template <int WT> struct BTile {
       kt0 += 2;                                                                           \
     } while (kt0 < KT);                                                                   \
   } while (0)
+
+// k-major tiles: MBK rows of k, each 256 bf16 columns (512 bytes, 32 chunks
+// of 16 bytes); chunk c of row r sits at chunk c ^ kswz(r). An MFMA operand
+// (lane l: 8 consecutive k of column colbase + l % 32, k = 16 ks + 8 (l / 32)
+// + 0..7) comes from two ds_read_b64_tr_b16: in each group of 16 lanes, lane
+// j points at 4 columns (colbase + 16 (g % 2) + 4 (j % 4), g = l / 16) of row
+// 16 ks + 8 (g / 2) + j / 4 (+ 4 for the second read), and the read hands
+// lane i of the group the 4 values of column i from those 4 rows. The 8 rows
+// of one read then carry 8 distinct swizzles, so its 64-byte pieces land in
+// 8 distinct 64-byte bank groups.
+MOE_DEV int kswz(int r) { return ((r & 3) + 4 * ((r >> 3) & 1)) * 4; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+MOE_DEV bf16x8 kmajor_frag(uint32_t tile, int colbase, int ks, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int r = ks * 16 + 8 * (g >> 1) + (j >> 2);
+  const int col = colbase + 16 * (g & 1) + 4 * (j & 3);
+  // rows r and r + 4 share a swizzle (r % 4 and r / 8 agree)
+  const uint32_t off = (uint32_t)(((col >> 3) ^ kswz(r)) * 16 + (col & 7) * 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_s16x4*>((uintptr_t)(tile + (uint32_t)r * 512u + off)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_s16x4*>((uintptr_t)(tile + (uint32_t)(r + 4) * 512u + off)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Zero the k positions of an operand at or past `valid` (stage-relative):
+// lane l holds k = 16 ks + 8 (l / 32) + 0..7.
+MOE_DEV bf16x8 mask_k(bf16x8 v, int ks, int lane, int valid) {
+  const int n = valid - (ks * 16 + 8 * (lane >> 5));   // valid entries among the 8
+  u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t keep = n >= 2 * q + 2 ? 0xffffffffu : n == 2 * q + 1 ? 0x0000ffffu : 0u;
+    w[q] &= keep;
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
 
 // WIDE: the gathered activation rows are addressed with 64-bit per-lane
 // pointers (x larger than 2 GiB); otherwise with 32-bit offsets from x.
@@ -277,7 +345,19 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   bf16x8 fa[2][MI], fb[2][NI];
 
   // K >= 64, so there is at least one stage
+#define MOE_AADDR(K0) (abase + (K0) * 2)
+#define MOE_BADDR(K0) (bbase + (K0) * ESZ)
+#define MOE_LOADA MOE_LOADA_ROWS
+#define MOE_LOADB MOE_LOADB_ROWS
+#define MOE_PRE_MFMA(SLOT, KT_, KS)
+#define MOE_READS_AFTER(q) ((q) < MI + NI ? 1 : 0)
   MOE_PIPELINE(K / MBK);
+#undef MOE_AADDR
+#undef MOE_BADDR
+#undef MOE_LOADA
+#undef MOE_LOADB
+#undef MOE_PRE_MFMA
+#undef MOE_READS_AFTER
 
   // epilogue; 32x32 accumulator layout: lane l holds column l%32, register
   // v holds row 8*(v/4) + 4*(l/32) + v%4
@@ -331,68 +411,69 @@ hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// weight gradients of the backward: per expert e,
-//   C_e[m][n] = sum over k in [p_e, p_(e+1)) of A[m][k] * B[n][k]
-// with A [M][ld] and B [N][ld] the transposed activations (token rows as k),
-// each expert's k range padded with zeros to a multiple of MBK (p_e is the
-// padded exclusive scan of the expert row counts, so every stage is whole).
-// Rows m < m_split go to out0 [E][m_split][N], the rest to out1
-// [E][M - m_split][N], bf16. Tiles: MT x NT per expert; a group of tiles
-// that share one operand block (the MT m tiles of one n tile when m_fast,
-// else the NT n tiles of one m tile) stays on one XCD, and the XCDs take
-// groups in turn, so a heavy expert is spread over all of them.
+// backward products on operands as they lie in HBM (no transposed copies)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(MNW * 64) void wgrad_mfma_kernel(WgradArgs w) {
-  constexpr bool I8 = false, WIDE = false;
+// Weight gradients: per expert e,
+//   C_e[m][n] = sum over the expert's dispatch rows r of a[r][m] * b[r][n],
+// both operands row-major over the dispatch rows (dy and h for dW_down,
+// [dg | du] and the gathered x rows for dW_gate|dW_up), so both are k-major
+// tiles read through transposing LDS reads. The last stage of an expert
+// reads up to 63 rows past its end (the buffers keep 64 rows of slack after
+// the last dispatch row); those k positions are zeroed in both operands
+// before the MFMAs. Tiles: MT x NT per expert; a group of tiles that share one operand block
+// (the MT m tiles of one n tile when m_fast, else the NT n tiles of one m
+// tile) stays on one XCD, and the XCDs take groups in turn, so a heavy
+// expert is spread over all of them. Rows m < m_split go to out0
+// [E][m_split][N], the rest to out1 [E][M - m_split][N], bf16.
+__global__ __launch_bounds__(MNW * 64) void wgrad_tn_kernel(WgradTnArgs w) {
+  constexpr bool WIDE = false;
   constexpr int CH = MBK / 8, NKS = MBK / 16;
-  constexpr int ESZ = 2, BCH = BTile<WT_BF16>::BCH, LPWB = BTile<WT_BF16>::LPW;
+  constexpr int BCH = BTile<WT_BF16>::BCH, LPWB = BTile<WT_BF16>::LPW;
   constexpr int MWM = WaveGrid<WT_BF16>::M, MWN = WaveGrid<WT_BF16>::N;
   constexpr int MW = MBM / MWM, NWR = MNB / MWN;
   constexpr int MI = MW / 32, NI = NWR / 32;
   __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
-  u32x4* const SA[2] = {sT0, sT1};
-  u32x4* const SB[2] = {sT0 + MBM * CH, sT1 + MBM * CH};
   const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
   const char* const* aptr = nullptr;
 
   const uint32_t MT = (uint32_t)(w.M + MBM - 1) / MBM, NT = (uint32_t)(w.N + MNB - 1) / MNB;
   const uint32_t G = w.m_fast ? MT : NT;
-  const uint32_t slot = blockIdx.x >> 3;
-  const uint32_t lin = ((slot / G) * 8 + (blockIdx.x & 7)) * G + slot % G;
+  const uint32_t slot_ = blockIdx.x >> 3;
+  const uint32_t lin = ((slot_ / G) * 8 + (blockIdx.x & 7)) * G + slot_ % G;
   if (lin >= (uint32_t)w.E * MT * NT) return;
   const int e = (int)(lin / (MT * NT));
   const uint32_t rem = lin % (MT * NT);
   const int mt = (int)(w.m_fast ? rem % MT : rem / NT);
   const int nt = (int)(w.m_fast ? rem / MT : rem % NT);
   const int m0 = mt * MBM, n0 = nt * MNB;
-  const int p0 = __builtin_amdgcn_readfirstlane(padded_start(w.offsets, e, MBK));
-  const int kt = (w.offsets[e + 1] - w.offsets[e] + MBK - 1) / MBK;
+  const int r0 = __builtin_amdgcn_readfirstlane(w.offsets[e]);
+  const int ne = __builtin_amdgcn_readfirstlane(w.offsets[e + 1]) - r0;
+  const int kt = (ne + MBK - 1) / MBK;
+  const int klast = ne - (kt - 1) * MBK;     // valid rows in the last stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const char* const abase =
-      uniform_ptr(static_cast<const char*>(w.a) + ((int64_t)m0 * w.ld + p0) * 2);
-  const char* const bbase =
-      uniform_ptr(static_cast<const char*>(w.b) + ((int64_t)n0 * w.ld + p0) * 2);
+  const char* const abase = uniform_ptr(static_cast<const char*>(w.a) + (int64_t)r0 * w.lda * 2);
+  const char* const bbase = uniform_ptr(static_cast<const char*>(w.b) + (int64_t)r0 * w.ldb * 2);
   uint32_t aoff[MLPW], boff[LPWB];
 #pragma unroll
   for (int j = 0; j < MLPW; ++j) {
     const int q = (MLPW * wave + j) * 64 + lane;
-    const int r = q / CH, c = (q % CH) ^ ((r >> 1) & 7);
-    aoff[j] = (uint32_t)(min(m0 + r, w.M - 1) - m0) * (uint32_t)(w.ld * 2) + c * 16;
+    const int kk = q >> 5, c = (q & 31) ^ kswz(kk);
+    aoff[j] = (uint32_t)kk * (uint32_t)(w.lda * 2) + (uint32_t)min(m0 + 8 * c, w.M - 8) * 2u;
   }
 #pragma unroll
   for (int j = 0; j < LPWB; ++j) {
     const int q = (LPWB * wave + j) * 64 + lane;
-    const int r = q / BCH, c = (q % BCH) ^ ((r >> 1) & 7);
-    boff[j] = (uint32_t)(min(n0 + r, w.N - 1) - n0) * (uint32_t)(w.ld * 2) + c * 16;
+    const int kk = q >> 5, c = (q & 31) ^ kswz(kk);
+    boff[j] = (uint32_t)kk * (uint32_t)(w.ldb * 2) + (uint32_t)min(n0 + 8 * c, w.N - 8) * 2u;
   }
   const int wm = wave / MWN, wn = wave % MWN;
-  int arow[MI], brow[NI];
+  int acol[MI], bcol[NI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) arow[mi] = wm * MW + mi * 32 + (lane & 31);
+  for (int mi = 0; mi < MI; ++mi) acol[mi] = wm * MW + mi * 32;
 #pragma unroll
-  for (int s = 0; s < NI; ++s) brow[s] = wn * NWR + s * 32 + (lane & 31);
+  for (int s = 0; s < NI; ++s) bcol[s] = wn * NWR + s * 32;
   f32x16 acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -400,11 +481,31 @@ __global__ __launch_bounds__(MNW * 64) void wgrad_mfma_kernel(WgradArgs w) {
     for (int s = 0; s < NI; ++s)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
-
   bf16x8 fa[2][MI], fb[2][NI];
 
+#define MOE_AADDR(K0) (abase + (int64_t)(K0) * w.lda * 2)
+#define MOE_BADDR(K0) (bbase + (int64_t)(K0) * w.ldb * 2)
+#define MOE_LOADA MOE_LOADA_KMAJOR
+#define MOE_LOADB MOE_LOADB_KMAJOR
+#define MOE_PRE_MFMA(SLOT, KT_, KS)                                              \
+  do {                                                                           \
+    if ((KT_) == KT - 1 && klast < MBK) {                                        \
+      _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                          \
+        fa[SLOT][mi] = mask_k(fa[SLOT][mi], (KS), lane, klast);                  \
+      _Pragma("unroll") for (int s = 0; s < NI; ++s)                             \
+        fb[SLOT][s] = mask_k(fb[SLOT][s], (KS), lane, klast);                    \
+    }                                                                            \
+  } while (0)
+// 12 reads per step after 8 MFMAs (other placements measured the same)
+#define MOE_READS_AFTER(q) ((q) < 4 ? 2 : 1)
   // an expert without rows has a zero gradient: no stage, zeros written
   if (kt > 0) MOE_PIPELINE(kt);
+#undef MOE_AADDR
+#undef MOE_BADDR
+#undef MOE_LOADA
+#undef MOE_LOADB
+#undef MOE_PRE_MFMA
+#undef MOE_READS_AFTER
 
   const int jcol = lane & 31;
 #pragma unroll
@@ -427,9 +528,110 @@ __global__ __launch_bounds__(MNW * 64) void wgrad_mfma_kernel(WgradArgs w) {
   }
 }
 
+// Data gradients: y[r][n] = sum_k a[r][k] * W_e[k][n] over the dispatch rows
+// r of each expert, with the weight used as it is stored (k-major rows:
+// W_down[e] is [H][F] for dh = dy W_down; for the dx rows, k < ksplit reads
+// W_gate[e] [F][H] and k >= ksplit W_up[e], against a = [dg | du]). The A
+// operand and the tiles are the down-mode kernel's; B is a k-major tile read
+// through transposing LDS reads.
+__global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_t n_ntiles) {
+  constexpr bool WIDE = false;
+  constexpr int CH = MBK / 8, NKS = MBK / 16;
+  constexpr int BCH = BTile<WT_BF16>::BCH, LPWB = BTile<WT_BF16>::LPW;
+  constexpr int MWM = WaveGrid<WT_BF16>::M, MWN = WaveGrid<WT_BF16>::N;
+  constexpr int MW = MBM / MWM, NWR = MNB / MWN;
+  constexpr int MI = MW / 32, NI = NWR / 32;
+  __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
+  u32x4* const SA[2] = {sT0, sT1};
+  const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
+  const char* const* aptr = nullptr;
+
+  uint32_t lin;
+  GroupedTile tile;
+  if (!xcd_tile_index(d.offsets, d.E, MBM, n_ntiles, lin)) return;
+  if (!grouped_tile(d.offsets, d.E, MBM, n_ntiles, lin, tile)) return;
+  const int e = __builtin_amdgcn_readfirstlane(tile.e);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile.m0);
+  const int m_end = __builtin_amdgcn_readfirstlane(tile.m_end);
+  const int n0 = __builtin_amdgcn_readfirstlane(tile.nt * MNB);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const char* const abase =
+      uniform_ptr(static_cast<const char*>(d.a) + (int64_t)m0 * d.K * 2);
+  uint32_t aoff[MLPW];
+#pragma unroll
+  for (int j = 0; j < MLPW; ++j) {
+    const int q = (MLPW * wave + j) * 64 + lane;
+    const int r = q / CH, c = (q % CH) ^ ((r >> 1) & 7);
+    aoff[j] = (uint32_t)(min(m0 + r, m_end - 1) - m0) * (uint32_t)(d.K * 2) + c * 16;
+  }
+  const char* const b0 = uniform_ptr(static_cast<const char*>(d.b0) +
+                                     (int64_t)e * d.ksplit * d.N * 2);
+  const char* const b1 = uniform_ptr(static_cast<const char*>(d.b1 ? d.b1 : d.b0) +
+                                     (int64_t)e * (d.K - d.ksplit) * d.N * 2);
+  uint32_t boff[LPWB];
+#pragma unroll
+  for (int j = 0; j < LPWB; ++j) {
+    const int q = (LPWB * wave + j) * 64 + lane;
+    const int kk = q >> 5, c = (q & 31) ^ kswz(kk);
+    boff[j] = (uint32_t)kk * (uint32_t)(d.N * 2) + (uint32_t)min(n0 + 8 * c, d.N - 8) * 2u;
+  }
+  const int wm = wave / MWN, wn = wave % MWN;
+  int arow[MI], bcol[NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) arow[mi] = wm * MW + mi * 32 + (lane & 31);
+#pragma unroll
+  for (int s = 0; s < NI; ++s) bcol[s] = wn * NWR + s * 32;
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int s = 0; s < NI; ++s)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
+  bf16x8 fa[2][MI], fb[2][NI];
+
+#define MOE_AADDR(K0) (abase + (K0) * 2)
+#define MOE_BADDR(K0)                                                          \
+  ((K0) < d.ksplit ? b0 + (int64_t)(K0) * d.N * 2                              \
+                   : b1 + (int64_t)((K0) - d.ksplit) * d.N * 2)
+#define MOE_LOADA MOE_LOADA_ROWS
+#define MOE_LOADB MOE_LOADB_KMAJOR
+#define MOE_PRE_MFMA(SLOT, KT_, KS)
+#define MOE_READS_AFTER(q) ((q) + MI * NI < MI + 2 * NI ? 2 : (q) < MI + 2 * NI ? 1 : 0)
+  MOE_PIPELINE(d.K / MBK);
+#undef MOE_AADDR
+#undef MOE_BADDR
+#undef MOE_LOADA
+#undef MOE_LOADB
+#undef MOE_PRE_MFMA
+#undef MOE_READS_AFTER
+
+  const int jcol = lane & 31;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = m0 + wm * MW + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (r >= m_end) continue;
+      uint16_t* yrow = static_cast<uint16_t*>(d.y) + (int64_t)r * d.N;
+#pragma unroll
+      for (int s = 0; s < NI; ++s) {
+        const int n = n0 + wn * NWR + s * 32 + jcol;
+        if (n < d.N) yrow[n] = f32_to_bf16_bits(acc[mi][s][v]);
+      }
+    }
+  }
+}
+
 #undef MOE_PIPELINE
 #undef MOE_ISSUE
 #undef MOE_LOADF
+#undef MOE_LOADA_ROWS
+#undef MOE_LOADB_ROWS
+#undef MOE_LOADA_KMAJOR
+#undef MOE_LOADB_KMAJOR
 
 // 32-bit offsets from x reach the gathered rows while x is below 2 GiB
 bool x_needs_wide(const FfnArgs& a) { return (uint64_t)a.T * (uint64_t)a.H * 2 > (1ull << 31); }
@@ -466,16 +668,20 @@ hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s) {
                          : launch_mfma<M_GATEUP_SAVE, WT_BF16, false>(a, s);
 }
 
-unsigned wgrad_grid(const WgradArgs& w) {
+hipError_t launch_wgrad_tn(const WgradTnArgs& w, hipStream_t s) {
   const unsigned MT = (unsigned)(w.M + MBM - 1) / MBM, NT = (unsigned)(w.N + MNB - 1) / MNB;
   const unsigned G = w.m_fast ? MT : NT;
   const unsigned groups = (unsigned)w.E * MT * NT / G;
-  return (groups + 7) / 8 * 8 * G;
-}
-
-hipError_t launch_wgrad(const WgradArgs& w, hipStream_t s) {
-  hipLaunchKernelGGL(wgrad_mfma_kernel, dim3(wgrad_grid(w)), dim3(MNW * 64), 0, s, w);
+  hipLaunchKernelGGL(wgrad_tn_kernel, dim3((groups + 7) / 8 * 8 * G), dim3(MNW * 64), 0, s, w);
   return hipGetLastError();
 }
+
+hipError_t launch_dgrad_nn(const DgradArgs& d, hipStream_t s) {
+  const uint32_t nt = (uint32_t)((d.N + MNB - 1) / MNB);
+  hipLaunchKernelGGL(dgrad_nn_kernel, dim3(grouped_grid(d.T * d.k, d.E, MBM, nt)),
+                     dim3(MNW * 64), 0, s, d, nt);
+  return hipGetLastError();
+}
+
 
 }  // namespace moe

@@ -58,14 +58,6 @@ MOE_DEV bool xcd_tile_index(const int32_t* __restrict__ offsets, int E, int BM,
   return true;
 }
 
-// Start of expert e's segment in a layout where every expert's rows are
-// padded up to a multiple of `seg`: sum over e' < e of n_e' rounded up.
-MOE_DEV int padded_start(const int32_t* __restrict__ offsets, int e, int seg) {
-  int p = 0;
-  for (int i = 0; i < e; ++i) p += (offsets[i + 1] - offsets[i] + seg - 1) / seg * seg;
-  return p;
-}
-
 // Worst-case grid, a multiple of 8 (see xcd_tile_index).
 inline unsigned grouped_grid(int64_t n_assign, int E, int BM, int n_ntiles) {
   const int64_t mt = (n_assign + BM - 1) / BM + E;

@@ -70,20 +70,37 @@ hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s);
 // with H, F, h, wd, y standing for the product's N, K, A, B and output)
 hipError_t launch_dgrad_tiled(const FfnArgs& a, hipStream_t s);
 
-// Backward weight-gradient GEMM (ffn_tiled.hip), bf16: per expert e,
-// C_e[m][n] = sum over the expert's padded k range of a[m][k] * b[n][k].
-struct WgradArgs {
-  const void* a;          // [M][ld]
-  const void* b;          // [N][ld]
-  int64_t ld;             // elements per row of a and b (256 * ld * 2 < 2^32)
-  const int32_t* offsets; // [E+1] dispatch offsets; expert e's k range starts
-                          // at the exclusive scan of the counts rounded up to 64
-  int E, M, N, m_split;
+// Weight gradients on row-major operands (ffn_tiled.hip): per expert e,
+// C_e[m][n] = sum over e's dispatch rows r of a[r][m] * b[r][n]. a and b
+// must stay readable for 63 rows past the last dispatch row (those rows are
+// read and masked out).
+struct WgradTnArgs {
+  const void* a;          // [rows][lda] bf16
+  int64_t lda;            // elements per row of a (>= M)
+  const void* b;          // [rows][ldb] bf16
+  int64_t ldb;            // elements per row of b (>= N)
+  const int32_t* offsets; // [E+1] dispatch offsets
+  int E, M, N, m_split;   // M, N multiples of 64
   void* out0;             // [E][m_split][N] bf16
   void* out1;             // [E][M - m_split][N] bf16 (unused when m_split == M)
   int m_fast;             // 1: tiles sharing a B block run together
 };
-hipError_t launch_wgrad(const WgradArgs& w, hipStream_t s);
+hipError_t launch_wgrad_tn(const WgradTnArgs& w, hipStream_t s);
+
+// Data gradients on the stored weights (ffn_tiled.hip): for every expert's
+// dispatch rows r, y[r][n] = sum_k a[r][k] W_e[k][n], W_e[k] row k of b0[e]
+// ([ksplit][N]) for k < ksplit, else row k - ksplit of b1[e] ([K-ksplit][N]).
+struct DgradArgs {
+  const void* a;          // [T*k][K] bf16
+  const int32_t* offsets; // [E+1]
+  int64_t T;
+  int E, k;
+  int N, K, ksplit;       // multiples of 64
+  const void* b0;
+  const void* b1;         // may be null when ksplit == K
+  void* y;                // [T*k][N] bf16
+};
+hipError_t launch_dgrad_nn(const DgradArgs& d, hipStream_t s);
 size_t decode_ws_bytes(int64_t T, int H, int k);
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
@@ -93,19 +110,7 @@ hipError_t launch_routing_stats(const float* logits, const int32_t* counts, int6
                                 int k, float* util, float* margin, float* mass, hipStream_t s);
 
 // backward of the layer (bwd.hip), bf16 activations and weights
-// rows of the padded per-expert layout of n_rows dispatch rows (each expert's
-// segment rounded up to 64; this bound holds for any split of the rows)
-int64_t bwd_padded_rows(int64_t n_rows, int E);
 int64_t router_wgrad_chunks(int64_t T);
-// dst[e][c][col0 + r] = src[e][r][c] for E matrices [R][C] (R, C multiples of 64)
-hipError_t launch_weight_transpose(const void* src, int E, int R, int C, void* dst, int64_t ldd,
-                                   int col0, hipStream_t s);
-// dst[c][p] (row stride ldd) for the padded layout of the dispatch rows; the
-// source row of dispatch row r is src + r*lds, or src + (perm[r]/k)*lds when
-// perm is given. C a multiple of 64.
-hipError_t launch_act_transpose(const void* src, int64_t lds, const int32_t* perm, int k,
-                                const int32_t* offsets, int E, int64_t n_rows, int C, void* dst,
-                                int64_t ldd, hipStream_t s);
 hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* slot_row,
                               const float* w, const int32_t* idx, int64_t T, int H, int E, int k,
                               void* dy, float* dw, float* dl, hipStream_t s);
