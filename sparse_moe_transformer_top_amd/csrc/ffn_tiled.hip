@@ -96,10 +96,8 @@ MOE_DEV void block_sync() {
 }
 
 // Modes of ffn_mfma_kernel. M_GATEUP_SAVE is M_GATEUP that also stores the
-// pre-activations g and u (bf16), which the backward reads. M_DGRAD is the
-// down-mode product as the backward uses it (dh, dx rows): the same code
-// under its own symbol, so that profiles tell it from the forward's.
-enum Mode { M_DOWN = 0, M_GATEUP = 1, M_GATEUP_SAVE = 2, M_DGRAD = 3 };
+// pre-activations g and u (bf16), which the backward reads.
+enum Mode { M_DOWN = 0, M_GATEUP = 1, M_GATEUP_SAVE = 2 };
 
 template <int WT> struct BTile {
   static constexpr int ESZ = WT == WT_I8 ? 1 : 2;       // weight element bytes
@@ -657,10 +655,6 @@ hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
   if (wt == WT_I4) return hipErrorNotSupported;
   return wt == WT_I8 ? launch_mfma<M_DOWN, WT_I8, false>(a, s)
                      : launch_mfma<M_DOWN, WT_BF16, false>(a, s);
-}
-
-hipError_t launch_dgrad_tiled(const FfnArgs& a, hipStream_t s) {
-  return launch_mfma<M_DGRAD, WT_BF16, false>(a, s);
 }
 
 hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s) {

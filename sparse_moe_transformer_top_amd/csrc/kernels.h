@@ -66,9 +66,6 @@ hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s);
 // bf16 gate/up that also writes g_save and u_save (training forward)
 hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s);
-// bf16 down-mode product y = h wd^T for the backward (dh and the dx rows,
-// with H, F, h, wd, y standing for the product's N, K, A, B and output)
-hipError_t launch_dgrad_tiled(const FfnArgs& a, hipStream_t s);
 
 // Weight gradients on row-major operands (ffn_tiled.hip): per expert e,
 // C_e[m][n] = sum over e's dispatch rows r of a[r][m] * b[r][n]. a and b
