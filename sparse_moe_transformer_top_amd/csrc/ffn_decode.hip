@@ -129,9 +129,10 @@ MOE_DEV void stream_steps(const uint16_t* arow, const char* const (&wrow)[NB], i
 }
 
 // int4 weights: the same round-robin steps (one scale group each). A step's
-// four MFMAs take the codes as bf16 128 + u; four more with a constant -136
-// operand remove the bias (u - 8 is the value), and the step's sum is scaled
-// by the row's group scale into the running sums.
+// four MFMAs take the codes as bf16 128 + u, starting from -136 times the
+// step's activations (four MFMAs against a constant operand, shared by all
+// weight rows), which removes the bias (u - 8 is the value); the step's sum
+// is scaled by the row's group scale into the running sums.
 template <int NB, int W, int kInFlight>
 MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB],
                              const float* const (&srow)[NB], int s_begin, int s_end, int wave,
@@ -160,18 +161,20 @@ MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB]
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       if (s0 + W * u < s_end) {
+        // -136 times the step's activations, once for all NB weight rows
+        f32x4 bias = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          bias = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][m]), as_bf16x8(cneg),
+                                                         bias, 0, 0, 0);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const uint32_t wd[4] = {bv[u][b].x, bv[u][b].y, bv[u][b].z, bv[u][b].w};
-          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+          f32x4 t = bias;
 #pragma unroll
           for (int m = 0; m < 4; ++m)
             t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 as_bf16x8(av[u][m]), as_bf16x8(u4x8_to_bf16x8_biased(wd[m])), t, 0, 0, 0);
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][m]), as_bf16x8(cneg), t,
-                                                        0, 0, 0);
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(sc[u][b], t[v], acc[b][v]);
         }
