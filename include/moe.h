@@ -316,7 +316,7 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
  *     then dx_t += dlogit_t W_router and dW_router = dlogit^T x.
  *
  * Supported: act_dtype = w_dtype = MOE_BF16 (else MOE_ERR_UNSUPPORTED),
- * T*k <= 2^22, and the shape limits above. The expert GEMMs always run on
+ * T*k < 2^31 - 64, and the shape limits above. The expert GEMMs always run on
  * the matrix-core tiles (no decode kernels), so out may differ from
  * moe_layer_forward's in the last bf16 bit when T <= 16.
  *

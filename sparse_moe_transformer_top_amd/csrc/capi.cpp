@@ -229,8 +229,8 @@ BwdWs bwd_ws_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E, int3
   return B;
 }
 
-// Training: bf16 activations and weights; the padded transposed layouts are
-// addressed with 32-bit offsets within a 256-row tile.
+// Training: bf16 activations and weights; row indices (with the 64 slack
+// rows) stay below 2^31.
 moe_status check_train(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k, moe_dtype act,
                        moe_dtype wt) {
   moe_status st;
@@ -239,8 +239,8 @@ moe_status check_train(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k, mo
   REQUIRE(act == MOE_BF16 && wt == MOE_BF16, MOE_ERR_UNSUPPORTED,
           "training entry points support bf16 activations and weights only (got %d, %d)",
           (int)act, (int)wt);
-  REQUIRE(T * (int64_t)k <= ((int64_t)1 << 22), MOE_ERR_UNSUPPORTED,
-          "training supports T*k <= 4194304 (got %lld)", (long long)(T * k));
+  REQUIRE(T * (int64_t)k + kBwdSlackRows < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+          "training supports T*k < 2^31 - 64 (got %lld)", (long long)(T * k));
   return ok();
 }
 
