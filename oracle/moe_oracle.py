@@ -1,8 +1,9 @@
 """Oracle for the top-2 MoE FFN layer -- TEST INFRASTRUCTURE ONLY.
 
-Plain, slow CPU reference of what the layer computes. Only the test suite, the
-graft smoke check and the benchmark's CPU-baseline leg may import it; the
-product path (the HIP library and its Python binding) never does.
+Plain, slow CPU reference of what the layer computes. Only the test suite,
+the smoke check (__graft_entry__.smoke) and the benchmark's CPU-baseline leg
+may import it; the product path (the HIP library and its Python binding)
+never does.
 
 Every function follows the n4n.ai page "How does Grok-1 use a
 mixture-of-experts design?" (cited below as "the page"), written from the
