@@ -246,6 +246,10 @@ def backward_workspace_bytes(T: int, H: int, F: int, E: int, k: int) -> int:
     return _lib.load().moe_layer_backward_workspace_bytes(T, H, F, E, k)
 
 
+# expert-FFN scratch in the training reserve (include/moe.h: 64 MiB)
+FFN_SCRATCH_BYTES = 64 << 20
+
+
 def _align256(n: int) -> int:
     return (n + 255) // 256 * 256
 
@@ -260,6 +264,7 @@ def train_reserve_views(reserve: torch.Tensor, T: int, H: int, F: int, E: int, k
              ("counts", torch.int32, (E,)), ("offsets", torch.int32, (E + 1,)),
              ("perm", torch.int32, (N,)), ("slot_row", torch.int32, (N,)),
              ("dropped", torch.uint8, (N,)), ("dispatch_scratch", torch.uint8, (disp_ws,)),
+             ("ffn_scratch", torch.uint8, (FFN_SCRATCH_BYTES,)),
              ("g", torch.bfloat16, (N, F)), ("u", torch.bfloat16, (N, F)),
              ("h", torch.bfloat16, (N + 64, F)), ("y_perm", torch.bfloat16, (N, H))]
     out, off = {}, 0

@@ -158,6 +158,7 @@ struct TrainReserve {
   int32_t* slot_row;
   uint8_t* dropped;
   void* dws;
+  void* fws;    // tile scratch of the down projection
   void* g;
   void* u;
   void* h;
@@ -189,6 +190,7 @@ TrainReserve train_reserve_layout(char* base, int64_t T, int32_t H, int32_t F, i
   R.slot_row = static_cast<int32_t*>(c.take(N * 4));
   R.dropped = static_cast<uint8_t*>(c.take(N));
   R.dws = c.take(dispatch_ws_bytes(T, E));
+  R.fws = c.take(tiled_ws_bytes());
   R.g = c.take((size_t)N * F * 2);
   R.u = c.take((size_t)N * F * 2);
   R.h = c.take((size_t)(N + kBwdSlackRows) * F * 2);
@@ -618,7 +620,7 @@ moe_status moe_layer_forward_train(const void* x, moe_dtype act_dtype, const flo
   if (e != hipSuccess) return hip_status(e, "dispatch launch");
   // the MFMA tiles at every T (the decode kernels keep no pre-activations)
   FfnArgs a{x, R.perm, R.offsets, T, H, F, E, k, w_gate, w_up, w_down, nullptr, nullptr, nullptr,
-            R.h, R.y, nullptr, R.g, R.u};
+            R.h, R.y, R.fws, R.g, R.u};
   e = launch_gateup_save_tiled(a, s);
   if (e != hipSuccess) return hip_status(e, "expert gate/up launch");
   e = launch_down_tiled(a, WT_BF16, s);

@@ -269,12 +269,22 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   u32x4* const SB[2] = {sT0 + MBM * CH, sT1 + MBM * CH};
   const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
 
-  uint32_t lin;
-  GroupedTile tile;
-  if (!xcd_tile_index(a.offsets, a.E, MBM, n_ntiles, lin)) return;
-  if (!grouped_tile(a.offsets, a.E, MBM, n_ntiles, lin, tile)) return;
   const int N = GATEUP ? a.F : a.H;
   const int K = GATEUP ? a.H : a.F;
+  uint32_t lin, pslot = 0;
+  int piece = -1, npieces = 1;
+  GroupedTile tile;
+  if (GATEUP) {
+    // (with 128 output columns per tile the Grok-1 shape's 256 column tiles
+    // fill whole rounds of every XCD)
+    if (!xcd_tile_index(a.offsets, a.E, MBM, n_ntiles, lin)) return;
+  } else {
+    if (!xcd_tail_work(a.offsets, a.E, MBM, n_ntiles, K / MBK, lin, piece, npieces, pslot)) return;
+  }
+  if (!grouped_tile(a.offsets, a.E, MBM, n_ntiles, lin, tile)) return;
+  // k stages of this work item (a piece of a split tail tile, or all)
+  const int kb = piece >= 0 ? piece * (K / MBK) / npieces : 0;
+  const int ke = piece >= 0 ? (piece + 1) * (K / MBK) / npieces : K / MBK;
   constexpr int BNO = GATEUP ? MNB / 2 : MNB;  // output columns per tile
   const int e = __builtin_amdgcn_readfirstlane(tile.e);
   const int m0 = __builtin_amdgcn_readfirstlane(tile.m0);
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   // goes into the scalar base.
   const char* const abase = GATEUP ? uniform_ptr(a.x)
                                    : uniform_ptr(static_cast<const char*>(a.h) +
-                                                 (int64_t)m0 * a.F * 2);
+                                                 (int64_t)m0 * a.F * 2 + (int64_t)kb * MBK * 2);
   uint32_t aoff[MLPW];
   const char* aptr[WIDE ? MLPW : 1];
 #pragma unroll
@@ -311,8 +321,8 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   // rows; with GATEUP, waves [0, MNW/2) load the gate rows (tile rows
   // [0, MNB/2)) and the others the up rows of the same output columns.
   const void* const wmat = GATEUP ? (wave < MNW / 2 ? a.wg : a.wu) : a.wd;
-  const char* const bbase =
-      uniform_ptr(static_cast<const char*>(wmat) + ((int64_t)e * N + n0) * K * ESZ);
+  const char* const bbase = uniform_ptr(static_cast<const char*>(wmat) +
+                                        (((int64_t)e * N + n0) * K + (int64_t)kb * MBK) * ESZ);
   uint32_t boff[LPWB];
 #pragma unroll
   for (int j = 0; j < LPWB; ++j) {
@@ -342,14 +352,14 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
       for (int v = 0; v < 16; ++v) acc[mi][s][v] = 0.f;
   bf16x8 fa[2][MI], fb[2][NI];
 
-  // K >= 64, so there is at least one stage
+  // K >= 64 and a piece holds >= 1 stage, so there is at least one stage
 #define MOE_AADDR(K0) (abase + (K0) * 2)
 #define MOE_BADDR(K0) (bbase + (K0) * ESZ)
 #define MOE_LOADA MOE_LOADA_ROWS
 #define MOE_LOADB MOE_LOADB_ROWS
 #define MOE_PRE_MFMA(SLOT, KT_, KS)
 #define MOE_READS_AFTER(q) ((q) < MI + NI ? 1 : 0)
-  MOE_PIPELINE(K / MBK);
+  MOE_PIPELINE(ke - kb);
 #undef MOE_AADDR
 #undef MOE_BADDR
 #undef MOE_LOADA
@@ -384,6 +394,12 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
             }
           }
         }
+      } else if (piece >= 0) {
+        // a piece of a split tail tile: float32 partial tile, summed and
+        // scaled by tail_reduce_kernel
+        float* prow = static_cast<float*>(a.ws) + (int64_t)pslot * MBM * MNB + (r - m0) * MNB;
+#pragma unroll
+        for (int s = 0; s < NI; ++s) prow[wn * NWR + s * 32 + jcol] = acc[mi][s][v];
       } else {
         uint16_t* yrow = static_cast<uint16_t*>(a.y) + (int64_t)r * a.H;
 #pragma unroll
@@ -398,13 +414,41 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   }
 }
 
+// The split tail tiles of a down-mode launch: y = the pieces' float32
+// partials summed in piece order (times the int8 row scale), rounded once.
+// One work-group per scratch slot's tile (XCD x, tail tile j).
+template <bool I8>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(FfnArgs a, uint32_t n_ntiles) {
+  const uint32_t xcd = blockIdx.x / kCusPerXcd, j = blockIdx.x % kCusPerXcd;
+  const TailPlan t = tail_plan(a.offsets, a.E, MBM, n_ntiles, xcd, a.F / MBK);
+  if (t.S <= 1 || j >= t.tail) return;
+  GroupedTile tile;
+  if (!grouped_tile(a.offsets, a.E, MBM, n_ntiles, t.base + t.full + j, tile)) return;
+  const int n0 = tile.nt * MNB;
+  const float* part = static_cast<const float*>(a.ws) +
+                      (int64_t)(xcd * kCusPerXcd + j * t.S) * MBM * MNB;
+  for (int idx = threadIdx.x; idx < MBM * MNB; idx += 256) {
+    const int r = tile.m0 + idx / MNB, n = n0 + idx % MNB;
+    if (r >= tile.m_end || n >= a.H) continue;
+    float v = 0.f;
+    for (uint32_t p = 0; p < t.S; ++p) v += part[(int64_t)p * MBM * MNB + idx];
+    if (I8) v *= a.sd[(int64_t)tile.e * a.H + n];
+    static_cast<uint16_t*>(a.y)[(int64_t)r * a.H + n] = f32_to_bf16_bits(v);
+  }
+}
+
 template <int MODE, int WT, bool WIDE>
 hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
   constexpr bool GATEUP = MODE == M_GATEUP || MODE == M_GATEUP_SAVE;
   const uint32_t nt = GATEUP ? (uint32_t)((a.F + MNB / 2 - 1) / (MNB / 2))
                              : (uint32_t)((a.H + MNB - 1) / MNB);
-  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WT, WIDE>),
-                     dim3(grouped_grid(a.T * a.k, a.E, MBM, nt)), dim3(MNW * 64), 0, s, a, nt);
+  const unsigned grid = grouped_grid(a.T * a.k, a.E, MBM, nt) + (GATEUP ? 0 : kTailExtraBlocks);
+  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WT, WIDE>), dim3(grid), dim3(MNW * 64), 0, s, a, nt);
+  if (GATEUP) return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((tail_reduce_kernel<WT == WT_I8>), dim3(8 * kCusPerXcd), dim3(256), 0, s, a,
+                     nt);
   return hipGetLastError();
 }
 
@@ -638,9 +682,13 @@ bool x_needs_wide(const FfnArgs& a) { return (uint64_t)a.T * (uint64_t)a.H * 2 >
 
 size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt) {
   (void)F; (void)E; (void)wt;
-  // the decode path keeps float32 split-k partials of the down projection
-  return (act == ACT_BF16 && T <= kDecodeMaxT) ? decode_ws_bytes(T, H, k) : 0;
+  // float32 split-k partials of the down projection: every tile's on the
+  // decode path, the split tail tiles' on the tiled path
+  if (act != ACT_BF16) return 0;
+  return T <= kDecodeMaxT ? decode_ws_bytes(T, H, k) : tiled_ws_bytes();
 }
+
+size_t tiled_ws_bytes() { return kTailScratchBytes; }
 
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
   if (wt == WT_I4) return hipErrorNotSupported;   // int4: decode kernels only

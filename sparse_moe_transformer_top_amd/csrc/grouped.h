@@ -58,6 +58,65 @@ MOE_DEV bool xcd_tile_index(const int32_t* __restrict__ offsets, int E, int BM,
   return true;
 }
 
+// Tail split. With one work-group per CU, an XCD's tiles run in rounds of
+// kCusPerXcd; when its count is not a multiple of that, the last round is
+// partial and most of the XCD waits for it. Those tail tiles are cut along k
+// into S = floor(kCusPerXcd / tail) pieces (at most max_pieces), so the last
+// round takes 1/S of a tile. Pieces write float32 partial tiles to scratch
+// slot (xcd, t) (t = slot - full, < kCusPerXcd); a reduce kernel adds them
+// in piece order. Work items of one XCD: slots [0, full) are whole tiles,
+// slots full + j*S + p are piece p of tail tile j.
+constexpr int kCusPerXcd = 32;   // MI355X: 256 CUs in 8 XCDs
+
+struct TailPlan {
+  uint32_t base;   // first real tile of this XCD
+  uint32_t full;   // whole tiles before the tail
+  uint32_t tail;   // tail tiles
+  uint32_t S;      // pieces per tail tile (1: the tail is not split)
+};
+
+MOE_DEV TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int BM, uint32_t n_ntiles,
+                           uint32_t xcd, int max_pieces) {
+  uint32_t R = 0;
+  for (int e = 0; e < E; ++e)
+    R += (uint32_t)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * n_ntiles;
+  const uint32_t per = (R + 7) / 8;
+  TailPlan t;
+  t.base = xcd * per;
+  const uint32_t cnt = R > t.base ? min(per, R - t.base) : 0u;
+  t.full = cnt / kCusPerXcd * kCusPerXcd;
+  t.tail = cnt - t.full;
+  t.S = t.tail ? min((uint32_t)max_pieces, max(1u, (uint32_t)kCusPerXcd / t.tail)) : 1u;
+  return t;
+}
+
+// This work-group's item: tile index lin, and piece (-1 for a whole tile) of
+// npieces, with its scratch slot. False for work-groups past the work.
+MOE_DEV bool xcd_tail_work(const int32_t* __restrict__ offsets, int E, int BM,
+                           uint32_t n_ntiles, int max_pieces, uint32_t& lin, int& piece,
+                           int& npieces, uint32_t& slot_out) {
+  const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const TailPlan t = tail_plan(offsets, E, BM, n_ntiles, xcd, max_pieces);
+  if (slot < t.full) {
+    lin = t.base + slot;
+    piece = -1;
+    npieces = 1;
+    return true;
+  }
+  const uint32_t q = slot - t.full;
+  if (q >= t.tail * t.S) return false;
+  lin = t.base + t.full + q / t.S;
+  npieces = (int)t.S;
+  piece = t.S > 1 ? (int)(q % t.S) : -1;
+  slot_out = xcd * kCusPerXcd + q;
+  return true;
+}
+
+// Extra work-groups a tail-split launch may need beyond the tile grid.
+constexpr unsigned kTailExtraBlocks = 8 * kCusPerXcd;
+// Float32 partial tiles of the split pieces (one 256 x 256 tile per slot).
+constexpr size_t kTailScratchBytes = (size_t)8 * kCusPerXcd * 256 * 256 * 4;
+
 // Worst-case grid, a multiple of 8 (see xcd_tile_index).
 inline unsigned grouped_grid(int64_t n_assign, int E, int BM, int n_ntiles) {
   const int64_t mt = (n_assign + BM - 1) / BM + E;

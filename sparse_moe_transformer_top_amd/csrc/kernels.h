@@ -43,7 +43,7 @@ struct FfnArgs {
   const float* sd;        // int8: [E,H]; int4: [E,H,F/128]
   void* h;                // [T*k,F] act
   void* y;                // [T*k,H] act
-  void* ws;
+  void* ws;               // decode: split-k partials; tiled down: tail partials
   void* g_save;           // [T*k,F] bf16 pre-activations (launch_gateup_save_tiled only)
   void* u_save;           // [T*k,F]
 };
@@ -59,6 +59,8 @@ size_t decode_lds_bytes(int64_t T, int H);
 hipError_t launch_gateup_decode_lds(const FfnArgs& a, Wt wt, hipStream_t s);
 
 size_t ffn_ws_bytes(int64_t T, int H, int F, int E, int k, Act act, Wt wt);
+// scratch of a tiled down-mode launch (float32 partials of its split tail tiles)
+size_t tiled_ws_bytes();
 // gate/up product with the SwiGLU epilogue (writes h) and down product (writes y)
 hipError_t launch_gateup_f32(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_f32(const FfnArgs& a, hipStream_t s);

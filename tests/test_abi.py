@@ -188,9 +188,11 @@ def test_layer_argument_errors(lib):
 def test_workspace_sizes(lib):
     T, H, F, E, k = 8192, 6144, 32768, 8, 2
     n = lib.moe_layer_workspace_bytes(T, H, F, E, k, BF16, BF16)
-    # h [T*k, F] and y_perm [T*k, H] in bf16 dominate
-    assert n >= T * k * (F + H) * 2
-    assert n < T * k * (F + H) * 2 + 64 * 2 ** 20
+    # h [T*k, F] and y_perm [T*k, H] in bf16 dominate; plus 64 MiB of
+    # float32 partials for the down projection's split tail tiles
+    assert n >= T * k * (F + H) * 2 + (64 << 20)
+    assert n < T * k * (F + H) * 2 + (128 << 20)
+    assert lib.moe_expert_ffn_workspace_bytes(T, H, F, E, k, BF16, BF16) == 64 << 20
     assert lib.moe_layer_workspace_bytes(T, H, F, E, k, F32, F32) > n
     assert lib.moe_layer_workspace_bytes(0, H, F, E, k, BF16, BF16) > 0
     assert lib.moe_expert_ffn_workspace_bytes(T, H, F, E, k, BF16, BF16) >= 0
@@ -238,7 +240,7 @@ def test_training_sizes(lib):
     N = T * k
     r = lib.moe_layer_train_reserve_bytes(T, H, F, E, k)
     # g, u, h [N, F] and y_perm [N, H] in bf16 dominate the reserve
-    assert N * (3 * F + H) * 2 <= r < N * (3 * F + H) * 2 + 16 * 2 ** 20   # h: + 64 rows
+    assert N * (3 * F + H) * 2 + (64 << 20) <= r < N * (3 * F + H) * 2 + (80 << 20)
     w = lib.moe_layer_backward_workspace_bytes(T, H, F, E, k)
     # dy, [dg | du] and the gathered x rows (64 slack rows each), dh and the
     # per-row dx, all bf16; no transposed weights

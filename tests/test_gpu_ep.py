@@ -5,8 +5,8 @@ The all-to-all is emulated by slicing device tensors on the host side of the
 test (rank r receives, from every source, the rows of its experts); every
 layout step and the experts run through the C ABI. Layouts are compared
 bit-exactly with the oracle's on the oracle's own dispatch; the EP output of
-every rank must equal the single-device layer (bitwise when both run the same
-GEMM kernel, else within the bf16 tolerance) and the oracle.
+every rank must equal the single-device layer and the oracle within the bf16
+tolerance.
 """
 import numpy as np
 import pytest
@@ -86,7 +86,6 @@ def test_ep_path_equals_layer(moe, R, name):
                         ecnt=np.diff(host_array(disp["offsets"]))))
     torch.cuda.synchronize()
     returned = {p: [] for p in range(R)}
-    all_tiled = True     # every destination's expert GEMMs took the tiled (T > 16) kernels
     sl = lambda t, e0, e1: None if t is None else t[e0:e1].contiguous()
     for r in range(R):
         parts, rc = [], np.zeros((R, El), np.int32)
@@ -96,7 +95,6 @@ def test_ep_path_equals_layer(moe, R, name):
             rc[p] = s["ecnt"][r * El:(r + 1) * El]
         recv = torch.cat(parts).contiguous()
         n_recv = recv.shape[0]
-        all_tiled &= n_recv == 0 or n_recv > 16
         off, ridx = moe.moe_ep_recv_layout(dev_tensor(rc, "i32"), n_recv)
         if n_recv:
             e0, e1 = r * El, (r + 1) * El
@@ -122,8 +120,5 @@ def test_ep_path_equals_layer(moe, R, name):
         res = oracle.layer_forward(xs, cfg.act, inp.wr, inp.wg, inp.wu, inp.wd, cfg.wdt, k=k,
                                    sg=inp.sg, su=inp.su, sd=inp.sd)
         check_close(out_as_f64(out), res.out, cfg.act, f"EP rank {p}")
-        if all_tiled and xs.shape[0] > 16:
-            # tiled GEMMs on both sides: per element, the same products in the same order
-            assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
-        else:
-            check_close(out_as_f64(out), out_as_f64(ref), cfg.act, f"EP rank {p} vs layer")
+        # (not bitwise: each side splits the k range of its own tail tiles)
+        check_close(out_as_f64(out), out_as_f64(ref), cfg.act, f"EP rank {p} vs layer")
