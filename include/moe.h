@@ -161,8 +161,8 @@ moe_status moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k
  * (BF16,I4).
  * ws: device scratch of at least moe_expert_ffn_workspace_bytes(...) bytes
  * (may be 0, then ws may be NULL; with bf16 activations it is the decode
- * path's split-k partials for T <= 16, else 64 MiB for the float32 partials
- * of the down projection's split tail tiles).
+ * path's split-k partials for T <= 16, else 192 MiB for the float32
+ * partials of the down projection's split tail tiles).
  * ------------------------------------------------------------------------ */
 size_t moe_expert_ffn_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                                       moe_dtype act_dtype, moe_dtype w_dtype);
@@ -329,7 +329,7 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
  *   boundary in this order: topk_idx [T,k] int32, topk_w [T,k] float32,
  *   counts [E] int32, offsets [E+1] int32, perm [T*k] int32, slot_row [T*k]
  *   int32, dropped [T*k] uint8 (all as moe_dispatch / moe_router_topk
- *   define them), dispatch scratch (moe_dispatch_workspace_bytes), 64 MiB of
+ *   define them), dispatch scratch (moe_dispatch_workspace_bytes), 192 MiB of
  *   expert-FFN scratch, then the
  *   bf16 pre-activations g [T*k,F] and u [T*k,F] (each rounded once from the
  *   float32 accumulator), h [T*k+64,F] and y_perm [T*k,H] (as
@@ -344,7 +344,8 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
  *   each output. ws: device scratch of moe_layer_backward_workspace_bytes
  *   (...) bytes, 16-byte aligned (it holds the row gradients dy, dh,
  *   [dg | du] and the per-row dx, and the x rows in dispatch order: about
- *   T*k*(3H + 3F)*2 bytes; the weights are used as stored, no transposed
+ *   T*k*(3H + 3F)*2 bytes, plus 192 MiB of float32 partial tiles for the
+ *   data-gradient products; the weights are used as stored, no transposed
  *   copies). The reserve is only read.
  * moe_layer_backward is exactly moe_layer_backward_data followed by
  *   moe_layer_backward_weights on one stream with the same reserve and ws:

@@ -246,8 +246,8 @@ def backward_workspace_bytes(T: int, H: int, F: int, E: int, k: int) -> int:
     return _lib.load().moe_layer_backward_workspace_bytes(T, H, F, E, k)
 
 
-# expert-FFN scratch in the training reserve (include/moe.h: 64 MiB)
-FFN_SCRATCH_BYTES = 64 << 20
+# expert-FFN scratch in the training reserve (include/moe.h: 192 MiB)
+FFN_SCRATCH_BYTES = 192 << 20
 
 
 def _align256(n: int) -> int:

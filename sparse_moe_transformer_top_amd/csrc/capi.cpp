@@ -210,6 +210,7 @@ struct BwdWs {
   float* dl;    // [T][E]
   float* part;  // router gradient partials
   int32_t* cnt; // [1] rows per rank of the gather (one rank)
+  void* tws;    // tile scratch of the data-gradient products
   size_t total;
 };
 
@@ -227,6 +228,7 @@ BwdWs bwd_ws_layout(char* base, int64_t T, int32_t H, int32_t F, int32_t E, int3
   B.dl = static_cast<float*>(c.take((size_t)T * E * 4));
   B.part = static_cast<float*>(c.take((size_t)router_wgrad_chunks(T) * E * h * 4));
   B.cnt = static_cast<int32_t*>(c.take(4));
+  B.tws = c.take(tiled_ws_bytes());
   B.total = c.off;
   return B;
 }
@@ -669,11 +671,11 @@ moe_status backward_data(const void* x, const float* w_router, const void* w_gat
   if (T > 0) {
     MOE_STEP(launch_combine_bwd(dout, R.y, R.slot_row, R.w, R.idx, T, H, E, k, B.dy, B.dw, B.dl,
                                 s), "combine backward launch");
-    const DgradArgs dh{B.dy, R.offsets, T, E, k, F, H, H, w_down, nullptr, B.dh};
+    const DgradArgs dh{B.dy, R.offsets, T, E, k, F, H, H, w_down, nullptr, B.dh, B.tws};
     MOE_STEP(launch_dgrad_nn(dh, s), "dh GEMM launch");
     MOE_STEP(launch_swiglu_bwd(B.dh, R.g, R.u, R.offsets, E, N, F, B.dgu, s),
              "SwiGLU backward launch");
-    const DgradArgs dxr{B.dgu, R.offsets, T, E, k, H, 2 * F, F, w_gate, w_up, B.dxr};
+    const DgradArgs dxr{B.dgu, R.offsets, T, E, k, H, 2 * F, F, w_gate, w_up, B.dxr, B.tws};
     MOE_STEP(launch_dgrad_nn(dxr, s), "dx GEMM launch");
     MOE_STEP(launch_dx_combine(B.dxr, R.slot_row, R.idx, B.dl, w_router, T, H, E, k, dx, s),
              "dx combine launch");

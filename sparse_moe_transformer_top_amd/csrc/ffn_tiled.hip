@@ -395,8 +395,8 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
           }
         }
       } else if (piece >= 0) {
-        // a piece of a split tail tile: float32 partial tile, summed and
-        // scaled by tail_reduce_kernel
+        // a piece of a split tail tile: float32 partial tile, summed (and
+        // scaled) by tail_reduce_kernel
         float* prow = static_cast<float*>(a.ws) + (int64_t)pslot * MBM * MNB + (r - m0) * MNB;
 #pragma unroll
         for (int s = 0; s < NI; ++s) prow[wn * NWR + s * 32 + jcol] = acc[mi][s][v];
@@ -414,27 +414,58 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   }
 }
 
-// The split tail tiles of a down-mode launch: y = the pieces' float32
-// partials summed in piece order (times the int8 row scale), rounded once.
-// One work-group per scratch slot's tile (XCD x, tail tile j).
-template <bool I8>
-__global__ __launch_bounds__(256) void tail_reduce_kernel(FfnArgs a, uint32_t n_ntiles) {
-  const uint32_t xcd = blockIdx.x / kCusPerXcd, j = blockIdx.x % kCusPerXcd;
-  const TailPlan t = tail_plan(a.offsets, a.E, MBM, n_ntiles, xcd, a.F / MBK);
-  if (t.S <= 1 || j >= t.tail) return;
+// The split tail tiles of a tail-split launch (the down projection, the data
+// gradients): y[r][n] = the pieces' float32 partials summed in piece order
+// (times scale[e][n] when scale is set), rounded once to bf16. A tail tile
+// is reduced by kReduceParts work-groups, one float4 of it per thread.
+struct TailReduce {
+  const int32_t* offsets;
+  int E;
+  int N;          // columns of y
+  int kstages;    // k stages of a whole tile (bounds the pieces)
+  const float* ws;
+  void* y;        // [rows][N] bf16
+  const float* scale;   // [E][N] or null
+};
+constexpr int kReduceParts = MBM * MNB / 4 / 256;
+
+__global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduce t, uint32_t n_ntiles) {
+  const uint32_t part = blockIdx.x % kReduceParts, tj = blockIdx.x / kReduceParts;
+  const uint32_t xcd = tj / kCusPerXcd, j = tj % kCusPerXcd;
+  const TailPlan p = tail_plan(t.offsets, t.E, MBM, n_ntiles, xcd, t.kstages);
+  if (p.S <= 1 || j >= p.tail) return;
   GroupedTile tile;
-  if (!grouped_tile(a.offsets, a.E, MBM, n_ntiles, t.base + t.full + j, tile)) return;
-  const int n0 = tile.nt * MNB;
-  const float* part = static_cast<const float*>(a.ws) +
-                      (int64_t)(xcd * kCusPerXcd + j * t.S) * MBM * MNB;
-  for (int idx = threadIdx.x; idx < MBM * MNB; idx += 256) {
-    const int r = tile.m0 + idx / MNB, n = n0 + idx % MNB;
-    if (r >= tile.m_end || n >= a.H) continue;
-    float v = 0.f;
-    for (uint32_t p = 0; p < t.S; ++p) v += part[(int64_t)p * MBM * MNB + idx];
-    if (I8) v *= a.sd[(int64_t)tile.e * a.H + n];
-    static_cast<uint16_t*>(a.y)[(int64_t)r * a.H + n] = f32_to_bf16_bits(v);
+  if (!grouped_tile(t.offsets, t.E, MBM, n_ntiles, p.base + p.full + j, tile)) return;
+  const int q = (int)part * 256 + (int)threadIdx.x;   // float4 of the tile
+  const int r = tile.m0 + q / (MNB / 4), n = tile.nt * MNB + (q % (MNB / 4)) * 4;
+  if (r >= tile.m_end || n >= t.N) return;
+  const float4* src = reinterpret_cast<const float4*>(t.ws) +
+                      (int64_t)(xcd * kTailSlots + j * p.S) * (MBM * MNB / 4) + q;
+  float4 v = src[0];
+#pragma unroll
+  for (uint32_t pc = 1; pc < kTailMaxPieces; ++pc) {
+    if (pc < p.S) {
+      const float4 w = src[(int64_t)pc * (MBM * MNB / 4)];
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
   }
+  const float o[4] = {v.x, v.y, v.z, v.w};
+  uint16_t* yrow = static_cast<uint16_t*>(t.y) + (int64_t)r * t.N;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (n + c >= t.N) break;
+    const float sc = t.scale ? t.scale[(int64_t)tile.e * t.N + n + c] : 1.f;
+    yrow[n + c] = f32_to_bf16_bits(t.scale ? o[c] * sc : o[c]);
+  }
+}
+
+hipError_t launch_tail_reduce(const TailReduce& t, uint32_t n_ntiles, hipStream_t s) {
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(8 * kCusPerXcd * kReduceParts), dim3(256), 0, s, t,
+                     n_ntiles);
+  return hipGetLastError();
 }
 
 template <int MODE, int WT, bool WIDE>
@@ -447,9 +478,9 @@ hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
   if (GATEUP) return hipGetLastError();
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((tail_reduce_kernel<WT == WT_I8>), dim3(8 * kCusPerXcd), dim3(256), 0, s, a,
-                     nt);
-  return hipGetLastError();
+  const TailReduce t{a.offsets, a.E, a.H, a.F / MBK, static_cast<const float*>(a.ws), a.y,
+                     WT == WT_I8 ? a.sd : nullptr};
+  return launch_tail_reduce(t, nt, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -574,8 +605,8 @@ __global__ __launch_bounds__(MNW * 64) void wgrad_tn_kernel(WgradTnArgs w) {
 // r of each expert, with the weight used as it is stored (k-major rows:
 // W_down[e] is [H][F] for dh = dy W_down; for the dx rows, k < ksplit reads
 // W_gate[e] [F][H] and k >= ksplit W_up[e], against a = [dg | du]). The A
-// operand and the tiles are the down-mode kernel's; B is a k-major tile read
-// through transposing LDS reads.
+// operand and the tiles are the down-mode kernel's, tail split included; B is
+// a k-major tile read through transposing LDS reads.
 __global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_t n_ntiles) {
   constexpr bool WIDE = false;
   constexpr int CH = MBK / 8, NKS = MBK / 16;
@@ -588,10 +619,16 @@ __global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_
   const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
   const char* const* aptr = nullptr;
 
-  uint32_t lin;
+  uint32_t lin, pslot = 0;
+  int piece = -1, npieces = 1;
   GroupedTile tile;
-  if (!xcd_tile_index(d.offsets, d.E, MBM, n_ntiles, lin)) return;
+  if (!xcd_tail_work(d.offsets, d.E, MBM, n_ntiles, d.K / MBK, lin, piece, npieces, pslot))
+    return;
   if (!grouped_tile(d.offsets, d.E, MBM, n_ntiles, lin, tile)) return;
+  // k range of this work item (a piece of a split tail tile, or all)
+  const int kb = piece >= 0 ? piece * (d.K / MBK) / npieces : 0;
+  const int ke = piece >= 0 ? (piece + 1) * (d.K / MBK) / npieces : d.K / MBK;
+  const int kofs = kb * MBK;
   const int e = __builtin_amdgcn_readfirstlane(tile.e);
   const int m0 = __builtin_amdgcn_readfirstlane(tile.m0);
   const int m_end = __builtin_amdgcn_readfirstlane(tile.m_end);
@@ -600,7 +637,7 @@ __global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const char* const abase =
-      uniform_ptr(static_cast<const char*>(d.a) + (int64_t)m0 * d.K * 2);
+      uniform_ptr(static_cast<const char*>(d.a) + (int64_t)m0 * d.K * 2 + (int64_t)kofs * 2);
   uint32_t aoff[MLPW];
 #pragma unroll
   for (int j = 0; j < MLPW; ++j) {
@@ -636,13 +673,13 @@ __global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_
 
 #define MOE_AADDR(K0) (abase + (K0) * 2)
 #define MOE_BADDR(K0)                                                          \
-  ((K0) < d.ksplit ? b0 + (int64_t)(K0) * d.N * 2                              \
-                   : b1 + (int64_t)((K0) - d.ksplit) * d.N * 2)
+  ((K0) + kofs < d.ksplit ? b0 + (int64_t)((K0) + kofs) * d.N * 2              \
+                          : b1 + (int64_t)((K0) + kofs - d.ksplit) * d.N * 2)
 #define MOE_LOADA MOE_LOADA_ROWS
 #define MOE_LOADB MOE_LOADB_KMAJOR
 #define MOE_PRE_MFMA(SLOT, KT_, KS)
 #define MOE_READS_AFTER(q) ((q) + MI * NI < MI + 2 * NI ? 2 : (q) < MI + 2 * NI ? 1 : 0)
-  MOE_PIPELINE(d.K / MBK);
+  MOE_PIPELINE(ke - kb);
 #undef MOE_AADDR
 #undef MOE_BADDR
 #undef MOE_LOADA
@@ -657,6 +694,12 @@ __global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_
     for (int v = 0; v < 16; ++v) {
       const int r = m0 + wm * MW + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (r >= m_end) continue;
+      if (piece >= 0) {
+        float* prow = static_cast<float*>(d.ws) + (int64_t)pslot * MBM * MNB + (r - m0) * MNB;
+#pragma unroll
+        for (int s = 0; s < NI; ++s) prow[wn * NWR + s * 32 + jcol] = acc[mi][s][v];
+        continue;
+      }
       uint16_t* yrow = static_cast<uint16_t*>(d.y) + (int64_t)r * d.N;
 #pragma unroll
       for (int s = 0; s < NI; ++s) {
@@ -720,9 +763,14 @@ hipError_t launch_wgrad_tn(const WgradTnArgs& w, hipStream_t s) {
 
 hipError_t launch_dgrad_nn(const DgradArgs& d, hipStream_t s) {
   const uint32_t nt = (uint32_t)((d.N + MNB - 1) / MNB);
-  hipLaunchKernelGGL(dgrad_nn_kernel, dim3(grouped_grid(d.T * d.k, d.E, MBM, nt)),
+  hipLaunchKernelGGL(dgrad_nn_kernel,
+                     dim3(grouped_grid(d.T * d.k, d.E, MBM, nt) + kTailExtraBlocks),
                      dim3(MNW * 64), 0, s, d, nt);
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const TailReduce t{d.offsets, d.E, d.N, d.K / MBK, static_cast<const float*>(d.ws), d.y,
+                     nullptr};
+  return launch_tail_reduce(t, nt, s);
 }
 
 

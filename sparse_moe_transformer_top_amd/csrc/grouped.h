@@ -61,12 +61,32 @@ MOE_DEV bool xcd_tile_index(const int32_t* __restrict__ offsets, int E, int BM,
 // Tail split. With one work-group per CU, an XCD's tiles run in rounds of
 // kCusPerXcd; when its count is not a multiple of that, the last round is
 // partial and most of the XCD waits for it. Those tail tiles are cut along k
-// into S = floor(kCusPerXcd / tail) pieces (at most max_pieces), so the last
-// round takes 1/S of a tile. Pieces write float32 partial tiles to scratch
-// slot (xcd, t) (t = slot - full, < kCusPerXcd); a reduce kernel adds them
-// in piece order. Work items of one XCD: slots [0, full) are whole tiles,
-// slots full + j*S + p are piece p of tail tile j.
-constexpr int kCusPerXcd = 32;   // MI355X: 256 CUs in 8 XCDs
+// into S pieces each (tail_pieces), so the tail takes ceil(tail S /
+// kCusPerXcd) rounds of 1/S of a tile instead of one whole tile. Pieces write
+// float32 partial tiles to scratch slot (xcd, q) (q = slot - full, below
+// kTailSlots); a reduce kernel adds them in piece order. Work items of one
+// XCD: slots [0, full) are whole tiles, slots full + j*S + p are piece p of
+// tail tile j.
+constexpr int kCusPerXcd = 32;             // MI355X: 256 CUs in 8 XCDs
+constexpr uint32_t kTailSlots = 96;        // partial tiles per XCD in scratch
+constexpr uint32_t kTailMaxPieces = 8;
+
+// Pieces per tail tile: over S <= min(kTailMaxPieces, max_pieces) with
+// tail * S <= kTailSlots, the S whose pieces finish first (ceil(tail S / 32)
+// / S of a tile), a larger S taken only for a gain of 10% or more over the
+// best smaller one (each piece adds a partial tile to write and read back).
+// 12 tail tiles: 5 pieces (0.4 of a tile); 24: 4 pieces (0.75).
+MOE_DEV uint32_t tail_pieces(uint32_t tail, uint32_t max_pieces) {
+  uint32_t best = 1, rounds = 1;   // the best time is rounds / best tiles
+  for (uint32_t S = 2; S <= kTailMaxPieces && S <= max_pieces && S * tail <= kTailSlots; ++S) {
+    const uint32_t r = (tail * S + kCusPerXcd - 1) / kCusPerXcd;
+    if (10 * r * best < 9 * rounds * S) {
+      best = S;
+      rounds = r;
+    }
+  }
+  return best;
+}
 
 struct TailPlan {
   uint32_t base;   // first real tile of this XCD
@@ -86,7 +106,7 @@ MOE_DEV TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int BM, u
   const uint32_t cnt = R > t.base ? min(per, R - t.base) : 0u;
   t.full = cnt / kCusPerXcd * kCusPerXcd;
   t.tail = cnt - t.full;
-  t.S = t.tail ? min((uint32_t)max_pieces, max(1u, (uint32_t)kCusPerXcd / t.tail)) : 1u;
+  t.S = t.tail ? tail_pieces(t.tail, (uint32_t)max_pieces) : 1u;
   return t;
 }
 
@@ -108,14 +128,15 @@ MOE_DEV bool xcd_tail_work(const int32_t* __restrict__ offsets, int E, int BM,
   lin = t.base + t.full + q / t.S;
   npieces = (int)t.S;
   piece = t.S > 1 ? (int)(q % t.S) : -1;
-  slot_out = xcd * kCusPerXcd + q;
+  slot_out = xcd * kTailSlots + q;
   return true;
 }
 
-// Extra work-groups a tail-split launch may need beyond the tile grid.
-constexpr unsigned kTailExtraBlocks = 8 * kCusPerXcd;
+// Extra work-groups a tail-split launch may need beyond the tile grid: per
+// XCD, full + tail S <= (its tiles) + kTailSlots.
+constexpr unsigned kTailExtraBlocks = 8 * kTailSlots;
 // Float32 partial tiles of the split pieces (one 256 x 256 tile per slot).
-constexpr size_t kTailScratchBytes = (size_t)8 * kCusPerXcd * 256 * 256 * 4;
+constexpr size_t kTailScratchBytes = (size_t)8 * kTailSlots * 256 * 256 * 4;
 
 // Worst-case grid, a multiple of 8 (see xcd_tile_index).
 inline unsigned grouped_grid(int64_t n_assign, int E, int BM, int n_ntiles) {

@@ -98,6 +98,7 @@ struct DgradArgs {
   const void* b0;
   const void* b1;         // may be null when ksplit == K
   void* y;                // [T*k][N] bf16
+  void* ws;               // tiled_ws_bytes() of scratch (split tail tiles)
 };
 hipError_t launch_dgrad_nn(const DgradArgs& d, hipStream_t s);
 size_t decode_ws_bytes(int64_t T, int H, int k);
