@@ -251,6 +251,66 @@ MOE_DEV bf16x8 mask_k(bf16x8 v, int ks, int lane, int valid) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// Output staging through LDS. Written straight from the 32x32 accumulator
+// layout, a 256 x 256 bf16 tile takes 128 two-byte stores per wave, and the
+// store instructions, not the bytes, bound the epilogue. Instead the tile
+// goes to the two LDS stages column-major ([n][m]: 256 rows of 512 bytes,
+// n < 128 in stage 0), each lane writing its 4 consecutive m of one column
+// as one 8-byte slot; slot (m / 4) of row n sits at (m / 4) ^ stage_swz(n).
+// Each lane then gathers 8 consecutive n of one m with two transposing
+// reads and writes them with one 16-byte store (16 per wave). Writes: the
+// 32 lanes of a half-wave cover 32 consecutive n at one m / 4, 32 distinct
+// slots mod 32, so all 64 banks once. Reads: 16-lane group g of a read
+// covers n = base + 32 g + 8 q + e (q, e < 4, +4 for the second read): the
+// low 4 bits of stage_swz take n's bits 0, 1, 3, 4 and bit 4 takes bit 2 ^
+// bit 5, so two groups again cover 32 distinct slots.
+MOE_DEV int stage_swz(int n) {
+  const int l = n & 31;
+  return ((l & 3) | ((l >> 1) & 0xC) | ((l & 4) << 2)) ^ (((n >> 5) & 1) << 4);
+}
+MOE_DEV uint32_t stage_addr(uint32_t L0, uint32_t L1, int n, int mq) {
+  return (n < 128 ? L0 + (uint32_t)n * 512u : L1 + (uint32_t)(n - 128) * 512u) +
+         (uint32_t)((mq ^ stage_swz(n)) * 8);
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+// rows 4 mq + 0..3 of column n (tile-local)
+MOE_DEV void stage_put4(uint32_t L0, uint32_t L1, int n, int mq, float a, float b, float c,
+                        float d) {
+  const u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  *reinterpret_cast<lds_u32x2*>((uintptr_t)stage_addr(L0, L1, n, mq)) = v;
+}
+// Read back for (mq, nb): this lane gets row 4 mq + (lane & 3), columns
+// nb + 32 (lane / 16) + 8 ((lane / 4) & 3) + 0..7 (returned via col).
+MOE_DEV uint4 stage_get8(uint32_t L0, uint32_t L1, int mq, int nb, int lane, int& row, int& col) {
+  const int g = lane >> 4, i = lane & 15;
+  // as a source of the transposing read: lane i points at n = ... + 8 (i % 4) + i / 4
+  const int n = nb + 32 * g + 8 * (i & 3) + (i >> 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_s16x4*>((uintptr_t)stage_addr(L0, L1, n, mq)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_s16x4*>((uintptr_t)stage_addr(L0, L1, n + 4, mq)));
+  row = 4 * mq + (i & 3);
+  col = nb + 32 * g + 8 * (i >> 2);
+  uint4 v;
+  v.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  v.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  v.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  v.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return v;
+}
+// every wave's LDS operand reads and direct loads done, then a barrier
+MOE_DEV void stage_begin() {
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  block_sync();
+}
+// the staged tile written, before the read-back
+MOE_DEV void stage_mid() {
+  wait_lgkmcnt0();
+  block_sync();
+}
+
 // WIDE: the gathered activation rows are addressed with 64-bit per-lane
 // pointers (x larger than 2 GiB); otherwise with 32-bit offsets from x.
 template <int MODE, int WT, bool WIDE>
@@ -580,24 +640,31 @@ __global__ __launch_bounds__(MNW * 64) void wgrad_tn_kernel(WgradTnArgs w) {
 #undef MOE_PRE_MFMA
 #undef MOE_READS_AFTER
 
-  const int jcol = lane & 31;
+  // epilogue through LDS (stage_put4 / stage_get8)
+  stage_begin();
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * MW + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (m >= w.M) continue;
-      uint16_t* const crow =
-          m < w.m_split
-              ? static_cast<uint16_t*>(w.out0) + ((int64_t)e * w.m_split + m) * w.N
-              : static_cast<uint16_t*>(w.out1) +
-                    ((int64_t)e * (w.M - w.m_split) + (m - w.m_split)) * w.N;
+    for (int s = 0; s < NI; ++s)
 #pragma unroll
-      for (int s = 0; s < NI; ++s) {
-        const int n = n0 + wn * NWR + s * 32 + jcol;
-        if (n < w.N) crow[n] = f32_to_bf16_bits(acc[mi][s][v]);
-      }
-    }
+      for (int j = 0; j < 4; ++j)
+        stage_put4(L0, L1, wn * NWR + s * 32 + (lane & 31), (wm * MW + mi * 32 + 8 * j) / 4 + (lane >> 5),
+                   acc[mi][s][4 * j], acc[mi][s][4 * j + 1], acc[mi][s][4 * j + 2],
+                   acc[mi][s][4 * j + 3]);
+  stage_mid();
+#pragma unroll 4
+  for (int it = 0; it < MBM * MNB / (MNW * 64 * 8); ++it) {
+    const int combo = it * MNW + wave;
+    int r, c;
+    const uint4 v = stage_get8(L0, L1, combo % (MBM / 4), combo / (MBM / 4) * 128, lane, r, c);
+    const int m = m0 + r, n = n0 + c;
+    if (m >= w.M || n >= w.N) continue;
+    uint16_t* const crow =
+        m < w.m_split
+            ? static_cast<uint16_t*>(w.out0) + ((int64_t)e * w.m_split + m) * w.N
+            : static_cast<uint16_t*>(w.out1) +
+                  ((int64_t)e * (w.M - w.m_split) + (m - w.m_split)) * w.N;
+    *reinterpret_cast<uint4*>(crow + n) = v;
   }
 }
 
