@@ -66,6 +66,37 @@ MOE_DEV u32x4 u4x8_to_bf16x8_biased(uint32_t w) {
   return r;
 }
 
+// Full-line weight streaming for v_mfma_f32_16x16x32_bf16, whose B operand
+// puts weight row i (of 16) in lanes i, i+16, i+32, i+48, each with 16 bytes
+// (8 k): a load per MFMA therefore covers only 64 bytes of each row, half of
+// every 128-byte line. Measured at the decode layout (12 KB rows), such
+// half-line loads stream 5.9 TB/s cached and 4.9 TB/s nontemporal, while
+// loads whose lanes cover whole lines reach 6.9 TB/s nontemporal. So a
+// "double step" (128 bytes = 64 k of each of 16 rows) is read by two loads,
+// load h covering rows 8h .. 8h+7 whole: lane (g, i) (g = lane / 16,
+// i = lane % 16) reads row 8h + i % 8 at 16-byte chunk g when (i < 8) ==
+// (h == 0), else at chunk 4 + g. The MFMA operand for the first 64 bytes
+// (chunk g of row i) is the lane's own load h = (i >= 8); for the second 64
+// bytes (chunk 4 + g) it is the other load of lane i ^ 8, a rotation by 8
+// lanes within each 16-lane row (DPP row_ror:8).
+MOE_DEV int dstep_chunk(int h, int i, int g) { return ((h == 0) == (i < 8)) ? g : 4 + g; }
+MOE_DEV u32x4 row_ror8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    r[q] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[q], 0x128, 0xF, 0xF, false);
+  return r;
+}
+// the two MFMA operands of a double step from its loads v0 (h = 0), v1 (h = 1)
+MOE_DEV void dstep_operands(u32x4 v0, u32x4 v1, int i, u32x4& first, u32x4& second) {
+  const bool lo = i < 8;
+  first = lo ? v0 : v1;
+  second = row_ror8(lo ? v1 : v0);
+}
+MOE_DEV u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 MOE_DEV bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 MOE_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

@@ -12,10 +12,13 @@
 // rows of one expert (the gate and up rows of the same 16 output columns for
 // kernel 1; 16 down rows and one k split for kernel 2); its waves take the
 // row's k steps round-robin, so at any time the waves of a work-group read
-// neighbouring 64-byte pieces of the same 128-byte lines, and each lane keeps
-// several 16-byte weight loads outstanding (InFlight). (Measured on MI355X at the
+// neighbouring pieces of the same rows, and each lane keeps several 16-byte
+// weight loads outstanding (InFlight). bf16 weights are read in 128-byte
+// double steps by nontemporal loads that each cover whole lines
+// (dstep_operands); int8 and int4 weights in 64-byte steps, whose two halves
+// of a line are read by neighbouring waves. (Measured on MI355X at the
 // Grok-1 shape: interleaved steps beat one contiguous k range per wave, and
-// nontemporal loads lose about a quarter of the bandwidth.) The products run
+// nontemporal loads of half lines lose about a quarter of the bandwidth.) The products run
 // on v_mfma_f32_16x16x32_bf16 with the expert's rows as the 16-row A operand
 // (rows past n_e are zero). The waves' partial sums are added in wave order
 // through LDS. int8 weights are loaded 16 per lane (64 k per step) and
@@ -94,6 +97,59 @@ MOE_DEV void mfma_step(const u32x4 (&av)[2], const u32x4 (&bv)[NB], f32x4 (&acc)
     for (int b = 0; b < NB; ++b)
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[0]), as_bf16x8(bv[b]), acc[b],
                                                        0, 0, 0);
+  }
+}
+
+// bf16 weights: accumulate this wave's double steps of [d_begin, d_end)
+// (64 k each; the wave takes d_begin + wave, + W, ...) of NB 16-row weight
+// tiles against the activation row arow (nullptr: zero row). wl[b][h] is
+// this lane's load h of tile b at double step 0 (dstep_chunk); g = lane / 16,
+// i = lane % 16.
+template <int NB, int W, int kInFlight>
+MOE_DEV void stream_dsteps_bf16(const uint16_t* arow, const char* const (&wl)[NB][2],
+                                int d_begin, int d_end, int wave, int i, int g,
+                                f32x4 (&acc)[NB]) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int d0 = d_begin + wave; d0 < d_end; d0 += W * kInFlight) {
+    u32x4 bv[kInFlight][NB][2];
+    u32x4 av[kInFlight][2];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int d = d0 + W * u;
+      if (d < d_end) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) bv[u][b][h] = ld16_nt(wl[b][h] + (int64_t)d * 128);
+        av[u][0] = arow ? ldg16(arow + 64 * d + 8 * g) : z;
+        av[u][1] = arow ? ldg16(arow + 64 * d + 32 + 8 * g) : z;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      if (d0 + W * u < d_end) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          u32x4 b0, b1;
+          dstep_operands(bv[u][b][0], bv[u][b][1], i, b0, b1);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][0]), as_bf16x8(b0),
+                                                           acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][1]), as_bf16x8(b1),
+                                                           acc[b], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// This lane's two loads (dstep_chunk) of the 16-row weight tile starting at
+// row n0 of a [rows][row_bytes] matrix at w (rows past the end clamped).
+MOE_DEV void dstep_addrs(const void* w, int64_t n0, int64_t rows, int64_t row_bytes, int i, int g,
+                         const char* (&wl)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t n = min(n0 + 8 * h + (i & 7), rows - 1);
+    wl[h] = static_cast<const char*>(w) + n * row_bytes + 16 * dstep_chunk(h, i, g);
   }
 }
 
@@ -209,7 +265,13 @@ __global__ __launch_bounds__(GateUpWaves<WT>::N * 64) void gateup_decode_kernel(
   f32x4 acc[2];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   acc[1] = acc[0];
-  {
+  if (WT == WT_BF16) {
+    const char* wl[2][2];
+    const int64_t r0w = (int64_t)e * a.F;   // the expert's first weight row
+    dstep_addrs(a.wg, r0w + n0, r0w + a.F, (int64_t)a.H * 2, i, g, wl[0]);
+    dstep_addrs(a.wu, r0w + n0, r0w + a.F, (int64_t)a.H * 2, i, g, wl[1]);
+    stream_dsteps_bf16<2, kWaves, InFlight<WT, 2>::N / 2>(arow, wl, 0, a.H / 64, wave, i, g, acc);
+  } else {
     const int64_t roff = ((int64_t)e * a.F + n) * a.H * Step<WT>::ESZ;
     const char* const wrow[2] = {static_cast<const char*>(a.wg) + roff,
                                  static_cast<const char*>(a.wu) + roff};
@@ -267,8 +329,14 @@ __global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnA
   f32x4 acc[1];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   int kb, ke;
-  split_range(a.F / Step<WT>::K, kSplit, split, kb, ke);
-  {
+  if (WT == WT_BF16) {
+    split_range(a.F / 64, kSplit, split, kb, ke);
+    const char* wl[1][2];
+    const int64_t r0w = (int64_t)e * a.H;
+    dstep_addrs(a.wd, r0w + n0, r0w + a.H, (int64_t)a.F * 2, i, g, wl[0]);
+    stream_dsteps_bf16<1, kWaves, InFlight<WT, 1>::N / 2>(arow, wl, kb, ke, wave, i, g, acc);
+  } else {
+    split_range(a.F / Step<WT>::K, kSplit, split, kb, ke);
     const char* const wrow[1] = {static_cast<const char*>(a.wd) +
                                  ((int64_t)e * a.H + n) * a.F * Step<WT>::ESZ};
     stream_steps<WT, 1, kWaves>(arow, wrow, kb, ke, wave, g, acc);

@@ -10,13 +10,13 @@
 // copies its expert's rows of x into LDS once (rows padded by 16 bytes, so
 // the 16 lanes that read one k chunk of 16 rows hit distinct banks) and each
 // of its 8 waves then owns one 16-column tile: it streams the tile's 16 gate
-// and 16 up weight rows on its own, keeping only weights in flight in its
-// registers (kXInFlight steps of 64 bytes per row), and takes the MFMA
+// and 16 up weight rows on its own with nontemporal full-line loads (see
+// dstep_operands), keeping only weights in flight in its registers
+// (kXInFlight double steps of 128 bytes per row), and takes the MFMA
 // activation operand from LDS. No cross-wave reduction: a wave's
-// accumulators hold its tile's sums over all of H. bf16 weights only:
-// measured at the Grok-1 decode shape it streams gate/up at 5.8 TB/s against
-// 5.6 TB/s for the waves-split-k kernel, while with int4 weights (whose
-// conversion and bias MFMAs sit between a wave's load batches) it was slower.
+// accumulators hold its tile's sums over all of H. bf16 weights only: with
+// int4 weights (whose conversion and bias MFMAs sit between a wave's load
+// batches) the split-k kernel was faster.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,7 +24,7 @@ namespace moe {
 namespace {
 
 constexpr int kXWaves = 8;        // waves per work-group = column tiles per work-group
-constexpr int kXInFlight = 8;     // 64-byte steps of each weight row in flight per lane
+constexpr int kXInFlight = 4;     // 128-byte double steps of each weight row in flight per lane
 constexpr int kXPad = 8;          // bf16 elements of padding per LDS row
 
 MOE_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -43,12 +43,16 @@ __global__ __launch_bounds__(kXWaves * 64) void gateup_xlds_kernel(FfnArgs a) {
   const int HP = a.H + kXPad;
   const int i = lane & 15, g = lane >> 4;
   const bool live = tile < tiles;
-  const int n = min(min(tile, tiles - 1) * 16 + i, a.F - 1);
-  const int64_t row = (int64_t)e * a.F + n;
   const int64_t row_bytes = (int64_t)a.H * 2;
-  const char* const wrow[2] = {static_cast<const char*>(a.wg) + row * row_bytes + 16 * g,
-                               static_cast<const char*>(a.wu) + row * row_bytes + 16 * g};
-  const int S = a.H / KS;
+  // this lane's two loads of each double step (dstep_chunk): rows 8h + i % 8
+  int64_t woff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = min(min(tile, tiles - 1) * 16 + 8 * h + (i & 7), a.F - 1);
+    woff[h] = ((int64_t)e * a.F + n) * row_bytes + 16 * dstep_chunk(h, i, g);
+  }
+  const char* const wmat[2] = {static_cast<const char*>(a.wg), static_cast<const char*>(a.wu)};
+  const int D = a.H / (2 * KS);
 
   // the expert's token rows into LDS, 16 bytes per thread and pass
   const int cpr = a.H / 8;
@@ -67,23 +71,33 @@ __global__ __launch_bounds__(kXWaves * 64) void gateup_xlds_kernel(FfnArgs a) {
   f32x4 acc[2];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   acc[1] = acc[0];
-  for (int s0 = 0; s0 < S; s0 += kXInFlight) {
-    u32x4 bv[kXInFlight][2];
+  for (int d0 = 0; d0 < D; d0 += kXInFlight) {
+    u32x4 bv[kXInFlight][2][2];   // [double step][gate, up][load h]
 #pragma unroll
     for (int u = 0; u < kXInFlight; ++u)
-      if (s0 + u < S) {
-        bv[u][0] = ld16(wrow[0] + (int64_t)(s0 + u) * 64);
-        bv[u][1] = ld16(wrow[1] + (int64_t)(s0 + u) * 64);
+      if (d0 + u < D) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bv[u][b][h] = ld16_nt(wmat[b] + woff[h] + (int64_t)(d0 + u) * 128);
       }
 #pragma unroll
     for (int u = 0; u < kXInFlight; ++u) {
-      if (s0 + u < S) {
-        // this lane group's 8 k of step s0+u: 16-byte chunk 4(s0+u) + g of the row
-        const u32x4 A = has_a ? xrow[4 * (s0 + u) + g] : z;
+      if (d0 + u < D) {
+        // this lane group's 8 k of the two 32-k halves: 16-byte chunks
+        // 8(d0+u) + g and 8(d0+u) + 4 + g of the activation row
+        const u32x4 A0 = has_a ? xrow[8 * (d0 + u) + g] : z;
+        const u32x4 A1 = has_a ? xrow[8 * (d0 + u) + 4 + g] : z;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A), as_bf16x8(bv[u][b]),
-                                                           acc[b], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) {
+          u32x4 B0, B1;
+          dstep_operands(bv[u][b][0], bv[u][b][1], i, B0, B1);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A0), as_bf16x8(B0), acc[b],
+                                                           0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A1), as_bf16x8(B1), acc[b],
+                                                           0, 0, 0);
+        }
       }
     }
   }
