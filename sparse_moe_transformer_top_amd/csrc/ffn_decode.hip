@@ -239,6 +239,73 @@ MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB]
   }
 }
 
+// int4 weights in double steps (two scale groups, 128 bytes of each row)
+// read by nontemporal full-line loads (dstep_operands): the operand of the
+// first group is the lane's own load, that of the second the rotated one;
+// each group as in stream_steps_i4. wl[b][h]: this lane's load h of tile b at
+// double step 0; srow[b]: the group scales of the lane's weight row of tile
+// b (row 16 t + i).
+template <int NB, int W, int kInFlight>
+MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wl)[NB][2],
+                              const float* const (&srow)[NB], int d_begin, int d_end, int wave,
+                              int i, int g, f32x4 (&acc)[NB]) {
+  constexpr uint32_t kNeg136 = 0xC308C308u;   // two bf16 -136.0
+  const u32x4 cneg = {kNeg136, kNeg136, kNeg136, kNeg136};
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int d0 = d_begin + wave; d0 < d_end; d0 += W * kInFlight) {
+    u32x4 bv[kInFlight][NB][2];
+    u32x4 av[kInFlight][2][4];
+    float sc[kInFlight][NB][2];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int d = d0 + W * u;
+      if (d < d_end) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            bv[u][b][h] = ld16_nt(wl[b][h] + (int64_t)d * 128);
+            sc[u][b][h] = srow[b][2 * d + h];
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = (2 * d + h) * 128 + 32 * g;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) av[u][h][m] = arow ? ldg16(arow + k + 8 * m) : z;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      if (d0 + W * u < d_end) {
+        u32x4 op[NB][2];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) dstep_operands(bv[u][b][0], bv[u][b][1], i, op[b][0], op[b][1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 bias = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            bias = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][h][m]),
+                                                           as_bf16x8(cneg), bias, 0, 0, 0);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const uint32_t wd[4] = {op[b][h].x, op[b][h].y, op[b][h].z, op[b][h].w};
+            f32x4 t = bias;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+              t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  as_bf16x8(av[u][h][m]), as_bf16x8(u4x8_to_bf16x8_biased(wd[m])), t, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(sc[u][b][h], t[v], acc[b][v]);
+          }
+        }
+      }
+    }
+  }
+}
+
 // contiguous share [b, e) of n steps for part p of parts
 MOE_DEV void split_range(int n, int parts, int p, int& b, int& e) {
   const int q = (n + parts - 1) / parts;
@@ -366,11 +433,15 @@ __global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnA
 // then serve the weight rows of all NT tiles, which cuts the activation
 // requests per weight byte by NT (with int4 codes the activations, 2 bytes
 // per code against half a byte of weight, were two thirds of the bytes a
-// work-group requested). Measured at the Grok-1 decode shape (T = 8): two
-// tiles with one step in flight per lane for gate/up (0.427 ms against 0.441
-// for one tile with two steps; four tiles, or two with two steps, cost
-// occupancy and were slower), two tiles with two steps for down (0.224 ms
-// against 0.266 for one tile with four).
+// work-group requested). Measured at the Grok-1 decode shape (T = 8) with
+// 64-byte steps: two tiles with one step in flight per lane for gate/up
+// (0.427 ms against 0.441 for one tile with two steps; four tiles, or two
+// with two steps, cost occupancy and were slower), two tiles with two steps
+// for down (0.224 ms against 0.266 for one tile with four). With full-line
+// double steps (stream_dsteps_i4, when the scale-group count is even): one
+// double step in flight, gate/up 0.354 ms and down 0.185 ms; one tile for
+// gate/up was within noise, two double steps in flight or one tile for down
+// were slower.
 #ifndef MOE_I4_GU_NT
 #define MOE_I4_GU_NT 2
 #endif
@@ -408,8 +479,21 @@ __global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64) void gateup_decode_i4_k
     acc[2 * t] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc[2 * t + 1] = acc[2 * t];
   }
-  stream_steps_i4<2 * NT, kWaves, InFlight<WT_I4, 2>::N>(arow, wrow, srow, 0, a.H / 128, wave, g,
-                                                         acc);
+  if ((a.H / 128) % 2 == 0) {
+    // full-line double steps (two scale groups)
+    const char* wl[2 * NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t r0w = (int64_t)e * a.F;
+      dstep_addrs(a.wg, r0w + n0 + 16 * t, r0w + a.F, a.H / 2, i, g, wl[2 * t]);
+      dstep_addrs(a.wu, r0w + n0 + 16 * t, r0w + a.F, a.H / 2, i, g, wl[2 * t + 1]);
+    }
+    stream_dsteps_i4<2 * NT, kWaves, InFlight<WT_I4, 2>::N>(arow, wl, srow, 0, a.H / 256, wave, i,
+                                                            g, acc);
+  } else {
+    stream_steps_i4<2 * NT, kWaves, InFlight<WT_I4, 2>::N>(arow, wrow, srow, 0, a.H / 128, wave,
+                                                           g, acc);
+  }
 #pragma unroll
   for (int b = 0; b < 2 * NT; ++b)
 #pragma unroll
@@ -462,8 +546,20 @@ __global__ __launch_bounds__(DownWaves<WT_I4>::N * 64) void down_decode_i4_kerne
     acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   int kb, ke;
-  split_range(a.F / 128, kSplit, split, kb, ke);
-  stream_steps_i4<NT, kWaves, InFlight<WT_I4, 1>::N>(arow, wrow, srow, kb, ke, wave, g, acc);
+  if ((a.F / 128) % 2 == 0) {
+    split_range(a.F / 256, kSplit, split, kb, ke);
+    const char* wl[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t r0w = (int64_t)e * a.H;
+      dstep_addrs(a.wd, r0w + n0 + 16 * t, r0w + a.H, a.F / 2, i, g, wl[t]);
+    }
+    stream_dsteps_i4<NT, kWaves, (InFlight<WT_I4, 1>::N + 1) / 2>(arow, wl, srow, kb, ke, wave, i,
+                                                                  g, acc);
+  } else {
+    split_range(a.F / 128, kSplit, split, kb, ke);
+    stream_steps_i4<NT, kWaves, InFlight<WT_I4, 1>::N>(arow, wrow, srow, kb, ke, wave, g, acc);
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
