@@ -100,19 +100,21 @@ MOE_DEV void mfma_step(const u32x4 (&av)[2], const u32x4 (&bv)[NB], f32x4 (&acc)
   }
 }
 
-// bf16 weights: accumulate this wave's double steps of [d_begin, d_end)
-// (64 k each; the wave takes d_begin + wave, + W, ...) of NB 16-row weight
-// tiles against the activation row arow (nullptr: zero row). wl[b][h] is
-// this lane's load h of tile b at double step 0 (dstep_chunk); g = lane / 16,
-// i = lane % 16.
-template <int NB, int W, int kInFlight>
-MOE_DEV void stream_dsteps_bf16(const uint16_t* arow, const char* const (&wl)[NB][2],
-                                int d_begin, int d_end, int wave, int i, int g,
-                                f32x4 (&acc)[NB]) {
+// bf16 or int8 weights: accumulate this wave's double steps of
+// [d_begin, d_end) (128 bytes of each weight row: 64 k bf16, 128 k int8; the
+// wave takes d_begin + wave, + W, ...) of NB 16-row weight tiles against the
+// activation row arow (nullptr: zero row). wl[b][h] is this lane's load h of
+// tile b at double step 0 (dstep_chunk); g = lane / 16, i = lane % 16. Each
+// half of a double step is one Step<WT> (mfma_step).
+template <int WT, int NB, int W, int kInFlight>
+MOE_DEV void stream_dsteps(const uint16_t* arow, const char* const (&wl)[NB][2], int d_begin,
+                           int d_end, int wave, int i, int g, f32x4 (&acc)[NB]) {
+  constexpr int KS = Step<WT>::K;
+  const int kl = WT == WT_I8 ? 16 * g : 8 * g;
   const u32x4 z = {0u, 0u, 0u, 0u};
   for (int d0 = d_begin + wave; d0 < d_end; d0 += W * kInFlight) {
     u32x4 bv[kInFlight][NB][2];
-    u32x4 av[kInFlight][2];
+    u32x4 av[kInFlight][2][2];   // [double step][half][A operand(s) of the half]
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       const int d = d0 + W * u;
@@ -121,22 +123,22 @@ MOE_DEV void stream_dsteps_bf16(const uint16_t* arow, const char* const (&wl)[NB
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int h = 0; h < 2; ++h) bv[u][b][h] = ld16_nt(wl[b][h] + (int64_t)d * 128);
-        av[u][0] = arow ? ldg16(arow + 64 * d + 8 * g) : z;
-        av[u][1] = arow ? ldg16(arow + 64 * d + 32 + 8 * g) : z;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = (2 * d + h) * KS + kl;
+          av[u][h][0] = arow ? ldg16(arow + k) : z;
+          av[u][h][1] = (WT == WT_I8 && arow) ? ldg16(arow + k + 8) : z;
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       if (d0 + W * u < d_end) {
+        u32x4 op[2][NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          u32x4 b0, b1;
-          dstep_operands(bv[u][b][0], bv[u][b][1], i, b0, b1);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][0]), as_bf16x8(b0),
-                                                           acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][1]), as_bf16x8(b1),
-                                                           acc[b], 0, 0, 0);
-        }
+        for (int b = 0; b < NB; ++b) dstep_operands(bv[u][b][0], bv[u][b][1], i, op[0][b], op[1][b]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) mfma_step<WT, NB>(av[u][h], op[h], acc);
       }
     }
   }
@@ -332,12 +334,15 @@ __global__ __launch_bounds__(GateUpWaves<WT>::N * 64) void gateup_decode_kernel(
   f32x4 acc[2];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   acc[1] = acc[0];
-  if (WT == WT_BF16) {
+  if (WT == WT_BF16 || (WT == WT_I8 && a.H % 128 == 0)) {
+    // full-line double steps of 128 bytes per row
     const char* wl[2][2];
     const int64_t r0w = (int64_t)e * a.F;   // the expert's first weight row
-    dstep_addrs(a.wg, r0w + n0, r0w + a.F, (int64_t)a.H * 2, i, g, wl[0]);
-    dstep_addrs(a.wu, r0w + n0, r0w + a.F, (int64_t)a.H * 2, i, g, wl[1]);
-    stream_dsteps_bf16<2, kWaves, InFlight<WT, 2>::N / 2>(arow, wl, 0, a.H / 64, wave, i, g, acc);
+    const int64_t rb = (int64_t)a.H * Step<WT>::ESZ;
+    dstep_addrs(a.wg, r0w + n0, r0w + a.F, rb, i, g, wl[0]);
+    dstep_addrs(a.wu, r0w + n0, r0w + a.F, rb, i, g, wl[1]);
+    stream_dsteps<WT, 2, kWaves, InFlight<WT, 2>::N / 2>(arow, wl, 0, (int)(rb / 128), wave, i, g,
+                                                         acc);
   } else {
     const int64_t roff = ((int64_t)e * a.F + n) * a.H * Step<WT>::ESZ;
     const char* const wrow[2] = {static_cast<const char*>(a.wg) + roff,
@@ -396,12 +401,13 @@ __global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnA
   f32x4 acc[1];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   int kb, ke;
-  if (WT == WT_BF16) {
-    split_range(a.F / 64, kSplit, split, kb, ke);
+  if (WT == WT_BF16 || (WT == WT_I8 && a.F % 128 == 0)) {
+    const int64_t rb = (int64_t)a.F * Step<WT>::ESZ;
+    split_range((int)(rb / 128), kSplit, split, kb, ke);
     const char* wl[1][2];
     const int64_t r0w = (int64_t)e * a.H;
-    dstep_addrs(a.wd, r0w + n0, r0w + a.H, (int64_t)a.F * 2, i, g, wl[0]);
-    stream_dsteps_bf16<1, kWaves, InFlight<WT, 1>::N / 2>(arow, wl, kb, ke, wave, i, g, acc);
+    dstep_addrs(a.wd, r0w + n0, r0w + a.H, rb, i, g, wl[0]);
+    stream_dsteps<WT, 1, kWaves, InFlight<WT, 1>::N / 2>(arow, wl, kb, ke, wave, i, g, acc);
   } else {
     split_range(a.F / Step<WT>::K, kSplit, split, kb, ke);
     const char* const wrow[1] = {static_cast<const char*>(a.wd) +
