@@ -46,6 +46,9 @@ CASES = [
     synth.get_config("p_bf16").with_(name="k1", T=200, E=4, k=1, seed=31),
     synth.get_config("p_cap").with_(name="k4cap", T=190, k=4, capacity_factor=0.5, seed=32,
                                     skew=(3.0, 2.5)),
+    # 40 column tiles in the dx-rows product and the forward down projection:
+    # whole rounds plus tail tiles split along k on every XCD
+    synth.get_config("p_bf16").with_(name="wide_tail", T=600, H=10240, F=256, seed=33),
 ]
 
 

@@ -50,6 +50,15 @@ SHAPES = [
     # rows too wide for LDS: falls back to the split-k decode kernel
     ("t8_wide_h", 8, 10240, 128, 8, 2, "bf16", "bf16", None),
     ("t8_i8_i4", 8, 384, 256, 8, 2, "bf16", "i4", None),
+    # 40 column tiles of the down projection per row tile: each XCD runs one
+    # whole round of 32 tiles and splits its 8 tail tiles along k (4 pieces)
+    ("t600_tail_split", 600, 10240, 256, 8, 2, "bf16", "bf16", None),
+    # decode weight streams: int8 rows that are not a multiple of 128 bytes
+    # (64-byte steps) next to full-line double steps, int4 with an odd number
+    # of scale groups in one matrix and an even number in the other
+    ("t5_i8_h320", 5, 320, 448, 8, 2, "bf16", "i8", None),
+    ("t9_i8_f576", 9, 512, 576, 8, 2, "bf16", "i8", None),
+    ("t8_i4_mixed", 8, 512, 640, 8, 2, "bf16", "i4", None),
 ]
 
 
