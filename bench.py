@@ -396,7 +396,7 @@ def main():
                 "traffic": traffic_from_profiles("gateup_decode", cfg.name),
                 "kernel": ("gateup_xlds_kernel (bf16 weights, token rows in LDS)"
                            if cfg.wdt == "bf16" and cfg.T <= 8 else
-                           "gateup_decode_i4_kernel (int4 weights, 2 column tiles per "
+                           "gateup_decode_i4_kernel (int4 weights, 4 column tiles per "
                            "work-group)" if cfg.wdt == "i4" else
                            "gateup_decode_kernel (%s weights)" % {
                                "bf16": "bf16", "i8": "int8"}[cfg.wdt]),

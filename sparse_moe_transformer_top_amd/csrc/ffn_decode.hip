@@ -445,16 +445,21 @@ __global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnA
 // with two steps, cost occupancy and were slower), two tiles with two steps
 // for down (0.224 ms against 0.266 for one tile with four). With full-line
 // double steps (stream_dsteps_i4, when the scale-group count is even): one
-// double step in flight, gate/up 0.354 ms and down 0.185 ms; one tile for
-// gate/up was within noise, two double steps in flight or one tile for down
-// were slower.
+// double step in flight, gate/up 0.354 ms and down 0.185 ms; then four
+// tiles for gate/up (the kernel already runs one work-group per CU, so the
+// extra registers cost no occupancy) 0.326 ms; one tile was within noise,
+// two double steps in flight, or four tiles for down, were slower.
 #ifndef MOE_I4_GU_NT
 #define MOE_I4_GU_NT 2
+#endif
+#ifndef MOE_I4_GU_NT_FULL
+#define MOE_I4_GU_NT_FULL 4
 #endif
 #ifndef MOE_I4_DN_NT
 #define MOE_I4_DN_NT 2
 #endif
-constexpr int kI4GateUpTiles = MOE_I4_GU_NT;
+constexpr int kI4GateUpTiles = MOE_I4_GU_NT;            // 64-byte steps
+constexpr int kI4GateUpTilesFull = MOE_I4_GU_NT_FULL;   // full-line double steps
 constexpr int kI4DownTiles = MOE_I4_DN_NT;
 
 template <int NT>
@@ -621,6 +626,11 @@ hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
   if (wt == WT_I8)
     hipLaunchKernelGGL(gateup_decode_kernel<WT_I8>, grid, dim3(GateUpWaves<WT_I8>::N * 64), 0, s,
                        a);
+  else if (wt == WT_I4 && (a.H / 128) % 2 == 0)   // the kernel takes double steps
+    hipLaunchKernelGGL(gateup_decode_i4_kernel<kI4GateUpTilesFull>,
+                       dim3((unsigned)(a.E * ((a.F + 16 * kI4GateUpTilesFull - 1) /
+                                              (16 * kI4GateUpTilesFull)))),
+                       dim3(GateUpWaves<WT_I4>::N * 64), 0, s, a);
   else if (wt == WT_I4)
     hipLaunchKernelGGL(gateup_decode_i4_kernel<kI4GateUpTiles>,
                        dim3((unsigned)(a.E * ((a.F + 16 * kI4GateUpTiles - 1) /
