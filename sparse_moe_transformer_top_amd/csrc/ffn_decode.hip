@@ -53,6 +53,10 @@ template <> struct DownWaves<WT_I4> { static constexpr int N = MOE_I4_DN_WAVES; 
 constexpr int kDownSplit = 8;
 template <int WT> struct DownSplit { static constexpr int N = kDownSplit; };
 template <> struct DownSplit<WT_I4> { static constexpr int N = MOE_I4_DOWN_SPLIT; };
+// the workspace (decode_ws_bytes) holds kDownSplit float32 partials per row
+static_assert(DownSplit<WT_BF16>::N <= kDownSplit && DownSplit<WT_I8>::N <= kDownSplit &&
+                  DownSplit<WT_I4>::N <= kDownSplit,
+              "a k split count above the workspace's kDownSplit partials");
 // k steps each lane keeps in flight, by weight type and number of weight
 // rows per lane (2: gate/up, 1: down). Measured at the Grok-1 decode shape:
 // the bf16 down projection streams about 9% faster with 8 steps than with 4;
