@@ -285,7 +285,9 @@ moe_status moe_ep_unpack(const void* y_rows, moe_dtype act_dtype, const int32_t*
  *   offsets [E+1] int32, dropped [T*k] uint8.
  * capacity_factor <= 0 or infinite: no capacity limit (inference).
  * ws: device scratch of at least moe_layer_workspace_bytes(...) bytes; it
- * holds the routing arrays, h and y_perm between the steps.
+ * holds the routing arrays, h and y_perm between the steps, and the expert
+ * FFN's scratch (moe_expert_ffn_workspace_bytes). Calls that overlap in time
+ * need workspaces of their own.
  * ------------------------------------------------------------------------ */
 size_t moe_layer_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                                  moe_dtype act_dtype, moe_dtype w_dtype);
