@@ -52,8 +52,39 @@ CASES = [
 ]
 
 
+def _random_cases(n=10, seed=77):
+    """Seeded random training shapes: expert counts 1 … 16, k up to 4, sizes
+    that are multiples of 64 but not of the 256-wide tiles, capacity factors
+    that drop and that do not, skewed and plain routers."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        E = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        T = int(rng.integers(1, 17)) if c % 4 == 0 else int(rng.integers(17, 500))
+        H = 64 * int(rng.integers(1, 11))
+        F = 64 * int(rng.integers(1, 13))
+        cf = [None, 0.5, 1.0, 1.25, 2.0][int(rng.integers(0, 5))]
+        skew = (float(rng.uniform(1, 3)), float(rng.uniform(0.5, 2))) if rng.random() < 0.3 else ()
+        cases.append(synth.LayerConfig(f"rb{c}_E{E}k{k}T{T}H{H}F{F}", T=T, H=H, F=F, E=E, k=k,
+                                       capacity_factor=cf, skew=skew, seed=2000 + c))
+    return cases
+
+
+RANDOM_CASES = _random_cases()
+
+
 @pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
 def test_backward_matches_oracle(moe, cfg):
+    _check_backward(moe, cfg)
+
+
+@pytest.mark.parametrize("cfg", RANDOM_CASES, ids=[c.name for c in RANDOM_CASES])
+def test_backward_random_shapes(moe, cfg):
+    _check_backward(moe, cfg)
+
+
+def _check_backward(moe, cfg):
     log(f"backward {cfg.name}: T={cfg.T} H={cfg.H} F={cfg.F} E={cfg.E} k={cfg.k} "
         f"cf={cfg.capacity_factor}")
     inp = synth.generate_host(cfg)
