@@ -49,6 +49,24 @@ def inputs(name):
 @pytest.mark.parametrize("name", ["decode", "prefill", "skew", "capacity", "decode_i4"])
 def test_fullsize_layer(moe, name):
     cfg, d = inputs(name)
+    _check_layer(moe, cfg, d, name)
+
+
+def test_x_beyond_2gib(moe):
+    # x larger than 2 GiB (180 000 tokens of 6144): the gate/up kernel
+    # addresses the gathered rows with 64-bit per-lane pointers instead of
+    # 32-bit offsets from x; a small F keeps h and the weights small
+    cfg = synth.LayerConfig("x_wide", T=180_000, H=6144, F=128, seed=51)
+    assert cfg.T * cfg.H * 2 > 2 ** 31
+    _weights.clear()
+    torch.cuda.empty_cache()
+    d = generate_device(cfg, "cuda")
+    _check_layer(moe, cfg, d, cfg.name)
+    del d
+    torch.cuda.empty_cache()
+
+
+def _check_layer(moe, cfg, d, name):
     log(f"full-size {name}: T={cfg.T} {cfg.act}/{cfg.wdt} cf={cfg.capacity_factor}")
     out, ax = moe.moe_layer_forward(d.x, d.wr, d.wg, d.wu, d.wd, k=cfg.k,
                                     capacity_factor=cfg.capacity_factor, s_gate=d.sg,
