@@ -173,9 +173,18 @@ def test_backward_empty_batch(moe):
         assert not g[n].float().abs().sum().item(), n
 
 
-def test_backward_at_grok1_training_shape(moe):
-    cfg = synth.CONFIGS["train"]
-    log(f"backward at the Grok-1 training shape: T={cfg.T} cf={cfg.capacity_factor}")
+# The Grok-1 training shape, and x above 2 GiB (4400 tokens of 245 760: the
+# saving gate/up kernel's 64-bit row pointers, 2 GB of gathered rows in the
+# backward) with a small F; the seed gives one tie-flagged token, so the
+# routing almost surely matches the oracle's.
+LARGE = [synth.CONFIGS["train"],
+         synth.LayerConfig("train_wide_x", T=4400, H=245_760, F=128, capacity_factor=1.25,
+                           seed=61)]
+
+
+@pytest.mark.parametrize("cfg", LARGE, ids=[c.name for c in LARGE])
+def test_backward_at_grok1_training_shape(moe, cfg):
+    log(f"backward at {cfg.name}: T={cfg.T} H={cfg.H} F={cfg.F} cf={cfg.capacity_factor}")
     dv = generate_device(cfg, "cuda")
     d = dict(x=dv.x, wr=dv.wr, wg=dv.wg, wu=dv.wu, wd=dv.wd)
     dout = grad_output_device(cfg.T, cfg.H, seed=cfg.seed)

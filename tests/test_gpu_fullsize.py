@@ -52,11 +52,12 @@ def test_fullsize_layer(moe, name):
     _check_layer(moe, cfg, d, name)
 
 
-def test_x_beyond_2gib(moe):
+@pytest.mark.parametrize("wdt", ["bf16", "i8"])
+def test_x_beyond_2gib(moe, wdt):
     # x larger than 2 GiB (180 000 tokens of 6144): the gate/up kernel
     # addresses the gathered rows with 64-bit per-lane pointers instead of
     # 32-bit offsets from x; a small F keeps h and the weights small
-    cfg = synth.LayerConfig("x_wide", T=180_000, H=6144, F=128, seed=51)
+    cfg = synth.LayerConfig("x_wide_" + wdt, T=180_000, H=6144, F=128, wdt=wdt, seed=51)
     assert cfg.T * cfg.H * 2 > 2 ** 31
     _weights.clear()
     torch.cuda.empty_cache()
