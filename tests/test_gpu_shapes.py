@@ -166,3 +166,24 @@ def test_gather_over_2gib_of_x(moe):
     check_close(out_as_f64(out)[sample][keep], res.out[keep], cfg.act, "x over 2 GiB")
     del d, out, ax
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["p_bf16_dec", "p_dec1", "p_i8_dec", "p_i4_dec", "p_i4_dec16"])
+def test_layer_forward_equals_stage_calls(moe, name):
+    # The layer forward equals, bitwise, its stage entry points run one after
+    # the other (router, dispatch, gate/up, down with its split-k reduce to
+    # y_perm, combine) on the decode kernels with every weight type.
+    cfg = synth.get_config(name)
+    log(f"layer vs stage calls {name}: T={cfg.T} {cfg.wdt} cf={cfg.capacity_factor}")
+    d = to_device(synth.generate_host(cfg))
+    out = moe.moe_layer_forward(d["x"], d["wr"], d["wg"], d["wu"], d["wd"], k=cfg.k,
+                                capacity_factor=cfg.capacity_factor, s_gate=d["sg"],
+                                s_up=d["su"], s_down=d["sd"])
+    idx, w = moe.moe_router_topk(d["x"], d["wr"], cfg.k)
+    disp = moe.moe_dispatch(idx, cfg.E, cfg.capacity_factor)
+    h = moe.moe_expert_gate_up(d["x"], disp["perm"], disp["offsets"], cfg.k, d["wg"], d["wu"],
+                               d["sg"], d["su"])
+    y = moe.moe_expert_down(h, disp["offsets"], cfg.T, cfg.k, d["wd"], d["sd"])
+    ref = moe.moe_combine(y, disp["slot_row"], w)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
