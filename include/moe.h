@@ -49,7 +49,8 @@
  *     u - 8. One float32 scale per row and group of 128 consecutive k:
  *     s_gate, s_up [E][F][H/128], s_down [E][H][F/128]; the effective weight
  *     is (u - 8) * s. Supported for T <= 16 (the decode kernels) with H and F
- *     multiples of 128; otherwise MOE_ERR_UNSUPPORTED.
+ *     multiples of 128 and one expert's codes under 2 GiB (H*F/2 < 2^31);
+ *     otherwise MOE_ERR_UNSUPPORTED.
  *   - Errors: every argument is checked before any HIP call; a failed check
  *     returns a non-zero status and enqueues nothing. A failed kernel launch
  *     returns MOE_ERR_HIP. moe_last_error() gives a message for the last

@@ -91,6 +91,10 @@ moe_status check_int4(int64_t T, int32_t H, int32_t F, moe_dtype w) {
           (long long)kDecodeMaxT, (long long)T);
   REQUIRE(H % 128 == 0 && F % 128 == 0, MOE_ERR_UNSUPPORTED,
           "MOE_I4 weights need H and F multiples of 128 (got H=%d F=%d)", H, F);
+  // the kernels address one expert's codes with 32-bit offsets
+  REQUIRE((int64_t)H * F / 2 < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+          "MOE_I4 weights need an expert matrix under 2 GiB (H*F/2 < 2^31, got H=%d F=%d)", H,
+          F);
   return ok();
 }
 

@@ -61,14 +61,33 @@ MOE_DEV u32x4 i8x8_to_bf16x8(uint32_t q0, uint32_t q1) {
 // Eight 4-bit codes u (one word; byte j holds element 2j in its low nibble
 // and element 2j+1 in its high nibble) -> eight bf16 values 128 + u, exact:
 // bf16 0x4300 is 128 with an empty 7-bit mantissa, which the code fills. The
-// caller removes the bias. Per output word: one byte permute, one and-or.
+// values come out in the element order 0, 2, 4, 6, 1, 3, 5, 7 (the MFMA's k
+// order within a lane is free as long as the activations take the same
+// order: bf16x8_even_odd). The low nibbles (even elements) and the high
+// nibbles (odd elements) are first split into one code per byte; a byte
+// permute then interleaves two codes with the exponent byte 0x43 taken from
+// a constant word: 7 VALU operations per word of codes. The caller removes
+// the bias.
 MOE_DEV u32x4 u4x8_to_bf16x8_biased(uint32_t w) {
-  const uint32_t s = w >> 4;   // byte j of s: element 2j+1 in its low nibble
+  const uint32_t ev = w & 0x0F0F0F0Fu;          // byte j: element 2j
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // byte j: element 2j + 1
+  constexpr uint32_t kExp = 0x43434343u;
   u32x4 r;
-  r.x = (__builtin_amdgcn_perm(s, w, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;
-  r.y = (__builtin_amdgcn_perm(s, w, 0x0C050C01u) & 0x000F000Fu) | 0x43004300u;
-  r.z = (__builtin_amdgcn_perm(s, w, 0x0C060C02u) & 0x000F000Fu) | 0x43004300u;
-  r.w = (__builtin_amdgcn_perm(s, w, 0x0C070C03u) & 0x000F000Fu) | 0x43004300u;
+  // selector bytes 0..3 pick bytes of the second operand, 4 the constant's
+  r.x = __builtin_amdgcn_perm(kExp, ev, 0x04010400u);   // elements 0, 2
+  r.y = __builtin_amdgcn_perm(kExp, ev, 0x04030402u);   // 4, 6
+  r.z = __builtin_amdgcn_perm(kExp, od, 0x04010400u);   // 1, 3
+  r.w = __builtin_amdgcn_perm(kExp, od, 0x04030402u);   // 5, 7
+  return r;
+}
+// Eight bf16 activations in element order 0 … 7 -> 0, 2, 4, 6, 1, 3, 5, 7,
+// the order of u4x8_to_bf16x8_biased's values.
+MOE_DEV u32x4 bf16x8_even_odd(u32x4 a) {
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(a.y, a.x, 0x05040100u);   // low halves: 0, 2
+  r.y = __builtin_amdgcn_perm(a.w, a.z, 0x05040100u);   // 4, 6
+  r.z = __builtin_amdgcn_perm(a.y, a.x, 0x07060302u);   // high halves: 1, 3
+  r.w = __builtin_amdgcn_perm(a.w, a.z, 0x07060302u);   // 5, 7
   return r;
 }
 
@@ -90,7 +109,7 @@ MOE_DEV u32x4 row_ror8(u32x4 v) {
   u32x4 r;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    r[q] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[q], 0x128, 0xF, 0xF, false);
+    r[q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[q], 0x128, 0xF, 0xF, false);
   return r;
 }
 // the two MFMA operands of a double step from its loads v0 (h = 0), v1 (h = 1)

@@ -31,6 +31,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -201,7 +203,6 @@ MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB]
                              int g, f32x4 (&acc)[NB]) {
   constexpr uint32_t kNeg136 = 0xC308C308u;   // two bf16 -136.0
   const u32x4 cneg = {kNeg136, kNeg136, kNeg136, kNeg136};
-  const u32x4 z = {0u, 0u, 0u, 0u};
   for (int s0 = s_begin + wave; s0 < s_end; s0 += W * kInFlight) {
     u32x4 bv[kInFlight][NB];
     u32x4 av[kInFlight][4];
@@ -217,12 +218,14 @@ MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB]
         }
         const int k = s * 128 + 32 * g;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) av[u][m] = arow ? ldg16(arow + k + 8 * m) : z;
+        for (int m = 0; m < 4; ++m) av[u][m] = ldg16(arow + k + 8 * m);
       }
     }
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       if (s0 + W * u < s_end) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) av[u][m] = bf16x8_even_odd(av[u][m]);
         // -136 times the step's activations, once for all NB weight rows
         f32x4 bias = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -245,19 +248,35 @@ MOE_DEV void stream_steps_i4(const uint16_t* arow, const char* const (&wrow)[NB]
   }
 }
 
+// This lane's two loads (dstep_chunk) of the 16-row int4 tile starting at
+// row n0 of an expert's [rows][row_bytes] matrix, as byte offsets from the
+// matrix start (rows past the end clamped; the matrix is under 2 GiB).
+MOE_DEV void dstep_offsets(int n0, int rows, int row_bytes, int i, int g, uint32_t (&wo)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = min(n0 + 8 * h + (i & 7), rows - 1);
+    wo[h] = (uint32_t)n * (uint32_t)row_bytes + 16u * (uint32_t)dstep_chunk(h, i, g);
+  }
+}
+
 // int4 weights in double steps (two scale groups, 128 bytes of each row)
 // read by nontemporal full-line loads (dstep_operands): the operand of the
 // first group is the lane's own load, that of the second the rotated one;
-// each group as in stream_steps_i4. wl[b][h]: this lane's load h of tile b at
-// double step 0; srow[b]: the group scales of the lane's weight row of tile
-// b (row 16 t + i).
-template <int NB, int W, int kInFlight>
-MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wl)[NB][2],
-                              const float* const (&srow)[NB], int d_begin, int d_end, int wave,
-                              int i, int g, f32x4 (&acc)[NB]) {
+// each group as in stream_steps_i4. NM matrices (gate and up, or down) share
+// the tiles' row offsets: matrix m of the expert starts at wb[m] (codes) and
+// sb[m] (group scales); wo[t][h] is this lane's load h of tile t at double
+// step 0 (dstep_offsets), so[t] the index of the first group scale of the
+// lane's weight row in tile t (row 16 t + i). Accumulator t NM + m holds
+// tile t of matrix m. The bases are uniform over the work-group, so each
+// load is a scalar base plus a 32-bit lane offset.
+template <int NT, int NM, int W, int kInFlight>
+MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wb)[NM],
+                              const uint32_t (&wo)[NT][2], const float* const (&sb)[NM],
+                              const uint32_t (&so)[NT], int d_begin, int d_end, int wave, int i,
+                              int g, f32x4 (&acc)[NT * NM]) {
+  constexpr int NB = NT * NM;
   constexpr uint32_t kNeg136 = 0xC308C308u;   // two bf16 -136.0
   const u32x4 cneg = {kNeg136, kNeg136, kNeg136, kNeg136};
-  const u32x4 z = {0u, 0u, 0u, 0u};
   for (int d0 = d_begin + wave; d0 < d_end; d0 += W * kInFlight) {
     u32x4 bv[kInFlight][NB][2];
     u32x4 av[kInFlight][2][4];
@@ -267,18 +286,21 @@ MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wl)[NB][
       const int d = d0 + W * u;
       if (d < d_end) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            bv[u][b][h] = ld16_nt(wl[b][h] + (int64_t)d * 128);
-            sc[u][b][h] = srow[b][2 * d + h];
+          for (int m = 0; m < NM; ++m) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              bv[u][t * NM + m][h] = ld16_nt(wb[m] + (wo[t][h] + (uint32_t)d * 128u));
+              sc[u][t * NM + m][h] = sb[m][so[t] + 2u * (uint32_t)d + (uint32_t)h];
+            }
           }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int k = (2 * d + h) * 128 + 32 * g;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) av[u][h][m] = arow ? ldg16(arow + k + 8 * m) : z;
+          for (int m = 0; m < 4; ++m) av[u][h][m] = ldg16(arow + k + 8 * m);
         }
       }
     }
@@ -290,6 +312,8 @@ MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wl)[NB][
         for (int b = 0; b < NB; ++b) dstep_operands(bv[u][b][0], bv[u][b][1], i, op[b][0], op[b][1]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) av[u][h][m] = bf16x8_even_odd(av[u][h][m]);
           f32x4 bias = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m)
@@ -310,6 +334,96 @@ MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wl)[NB][
       }
     }
   }
+}
+
+// The same double steps as stream_dsteps_i4, software-pipelined without a
+// second set of registers: right after tile b's codes of step d have been
+// rearranged into MFMA operands (dstep_operands), the loads of tile b for
+// the wave's next step go into the same registers, so the wave's next step
+// streams in while it converts and multiplies the rest of step d (the
+// conversion's VALU work is about half the time the loads take). The last
+// step is peeled, so every load in the loop is unconditional.
+template <int NT, int NM, int W>
+MOE_DEV void stream_dsteps_i4_roll(const uint16_t* arow, const char* const (&wb)[NM],
+                                   const uint32_t (&wo)[NT][2], const float* const (&sb)[NM],
+                                   const uint32_t (&so)[NT], int d_begin, int d_end, int wave,
+                                   int i, int g, f32x4 (&acc)[NT * NM]) {
+  constexpr int NB = NT * NM;
+  constexpr uint32_t kNeg136 = 0xC308C308u;   // two bf16 -136.0
+  const u32x4 cneg = {kNeg136, kNeg136, kNeg136, kNeg136};
+  int d = d_begin + wave;
+  if (d >= d_end) return;
+  u32x4 bv[NB][2];
+  float2 sc[NB];   // the two group scales of a double step (so[t] is even)
+  u32x4 av[2][4];
+  auto load_w = [&](int t, int m, int dd) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      bv[t * NM + m][h] = ld16_nt(wb[m] + (wo[t][h] + (uint32_t)dd * 128u));
+  };
+  auto load_s = [&](int t, int m, int dd) {
+    sc[t * NM + m] = *reinterpret_cast<const float2*>(sb[m] + so[t] + 2u * (uint32_t)dd);
+  };
+  auto load_a = [&](int dd) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) av[h][m] = ldg16(arow + (2 * dd + h) * 128 + 32 * g + 8 * m);
+  };
+  load_a(d);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      load_w(t, m, d);
+      load_s(t, m, d);
+    }
+  // one double step from the registers; with more, the loads of step dn
+  // replace each operand as soon as it has been consumed
+  auto step = [&](auto more, int dn) {
+    u32x4 a[2][4];
+    f32x4 bias[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bias[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        a[h][m] = bf16x8_even_odd(av[h][m]);
+        bias[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[h][m]), as_bf16x8(cneg),
+                                                          bias[h], 0, 0, 0);
+      }
+    }
+    if constexpr (decltype(more)::value) load_a(dn);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int b = t * NM + m;
+        u32x4 op[2];
+        dstep_operands(bv[b][0], bv[b][1], i, op[0], op[1]);
+        if constexpr (decltype(more)::value) load_w(t, m, dn);
+        const float s[2] = {sc[b].x, sc[b].y};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t wd[4] = {op[h].x, op[h].y, op[h].z, op[h].w};
+          f32x4 r = bias[h];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(a[h][q]), as_bf16x8(u4x8_to_bf16x8_biased(wd[q])), r, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(s[h], r[v], acc[b][v]);
+        }
+        // the scales are loaded once used, so no copy of them is kept
+        if constexpr (decltype(more)::value) load_s(t, m, dn);
+        // keep the tiles in order: hoisting a later tile's operand
+        // rearrangement would wait for all of the step's loads
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  for (; d + W < d_end; d += W) step(std::true_type{}, d + W);
+  step(std::false_type{}, 0);
 }
 
 // contiguous share [b, e) of n steps for part p of parts
@@ -479,8 +593,10 @@ __global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64) void gateup_decode_i4_k
   if (ne <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const uint16_t* arow = nullptr;
-  if (i < ne) arow = static_cast<const uint16_t*>(a.x) + (int64_t)(a.perm[r0 + i] / a.k) * a.H;
+  // lanes past the expert's rows repeat its last row: their output rows
+  // are never stored, and every lane's loads stay unconditional
+  const uint16_t* arow =
+      static_cast<const uint16_t*>(a.x) + (int64_t)(a.perm[r0 + min(i, ne - 1)] / a.k) * a.H;
   const char* wrow[2 * NT];
   const float* srow[2 * NT];
   f32x4 acc[2 * NT];
@@ -496,15 +612,16 @@ __global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64) void gateup_decode_i4_k
   }
   if ((a.H / 128) % 2 == 0) {
     // full-line double steps (two scale groups)
-    const char* wl[2 * NT][2];
+    const int64_t eb = (int64_t)e * a.F * (a.H / 2), es = (int64_t)e * a.F * (a.H / 128);
+    const char* wb[2] = {static_cast<const char*>(a.wg) + eb, static_cast<const char*>(a.wu) + eb};
+    const float* sb[2] = {a.sg + es, a.su + es};
+    uint32_t wo[NT][2], so[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int64_t r0w = (int64_t)e * a.F;
-      dstep_addrs(a.wg, r0w + n0 + 16 * t, r0w + a.F, a.H / 2, i, g, wl[2 * t]);
-      dstep_addrs(a.wu, r0w + n0 + 16 * t, r0w + a.F, a.H / 2, i, g, wl[2 * t + 1]);
+      dstep_offsets(n0 + 16 * t, a.F, a.H / 2, i, g, wo[t]);
+      so[t] = (uint32_t)min(n0 + 16 * t + i, a.F - 1) * (uint32_t)(a.H / 128);
     }
-    stream_dsteps_i4<2 * NT, kWaves, InFlight<WT_I4, 2>::N>(arow, wl, srow, 0, a.H / 256, wave, i,
-                                                            g, acc);
+    stream_dsteps_i4_roll<NT, 2, kWaves>(arow, wb, wo, sb, so, 0, a.H / 256, wave, i, g, acc);
   } else {
     stream_steps_i4<2 * NT, kWaves, InFlight<WT_I4, 2>::N>(arow, wrow, srow, 0, a.H / 128, wave,
                                                            g, acc);
@@ -548,8 +665,8 @@ __global__ __launch_bounds__(DownWaves<WT_I4>::N * 64) void down_decode_i4_kerne
   if (ne <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const uint16_t* arow = i < ne ? static_cast<const uint16_t*>(a.h) + (int64_t)(r0 + i) * a.F
-                                : nullptr;
+  // lanes past the expert's rows repeat its last row (never stored)
+  const uint16_t* arow = static_cast<const uint16_t*>(a.h) + (int64_t)(r0 + min(i, ne - 1)) * a.F;
   const char* wrow[NT];
   const float* srow[NT];
   f32x4 acc[NT];
@@ -563,14 +680,18 @@ __global__ __launch_bounds__(DownWaves<WT_I4>::N * 64) void down_decode_i4_kerne
   int kb, ke;
   if ((a.F / 128) % 2 == 0) {
     split_range(a.F / 256, kSplit, split, kb, ke);
-    const char* wl[NT][2];
+    const char* wb[1] = {static_cast<const char*>(a.wd) + (int64_t)e * a.H * (a.F / 2)};
+    const float* sb[1] = {a.sd + (int64_t)e * a.H * (a.F / 128)};
+    uint32_t wo[NT][2], so[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int64_t r0w = (int64_t)e * a.H;
-      dstep_addrs(a.wd, r0w + n0 + 16 * t, r0w + a.H, a.F / 2, i, g, wl[t]);
+      dstep_offsets(n0 + 16 * t, a.H, a.F / 2, i, g, wo[t]);
+      so[t] = (uint32_t)min(n0 + 16 * t + i, a.H - 1) * (uint32_t)(a.F / 128);
     }
-    stream_dsteps_i4<NT, kWaves, (InFlight<WT_I4, 1>::N + 1) / 2>(arow, wl, srow, kb, ke, wave, i,
-                                                                  g, acc);
+    // (the pipelined stream, stream_dsteps_i4_roll, needs 163 VGPRs here
+    // against 121, which halves the work-groups per CU: measured slower)
+    stream_dsteps_i4<NT, 1, kWaves, (InFlight<WT_I4, 1>::N + 1) / 2>(arow, wb, wo, sb, so, kb, ke,
+                                                                     wave, i, g, acc);
   } else {
     split_range(a.F / 128, kSplit, split, kb, ke);
     stream_steps_i4<NT, kWaves, InFlight<WT_I4, 1>::N>(arow, wrow, srow, kb, ke, wave, g, acc);

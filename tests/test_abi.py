@@ -103,6 +103,9 @@ def test_expert_ffn_argument_errors(lib):
     assert ffn(lib, wdt=I4, T=8, H=192, scales=(P, P, P)) == UNS
     assert ffn(lib, wdt=I4, T=8, F=320, scales=(P, P, P)) == UNS
     assert ffn(lib, act=F32, wdt=I4, T=8, scales=(P, P, P)) == UNS
+    # one expert's int4 codes must stay under 2 GiB (32-bit offsets in the kernels)
+    assert ffn(lib, wdt=I4, T=8, H=65536, F=65536, scales=(P, P, P)) == UNS
+    assert ffn(lib, wdt=I4, T=0, H=65536, F=65536, scales=(P, P, P)) == UNS
 
 
 def test_stage_entry_points_argument_errors(lib):
