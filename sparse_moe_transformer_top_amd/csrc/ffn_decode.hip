@@ -354,7 +354,7 @@ MOE_DEV void stream_dsteps_i4_roll(const uint16_t* arow, const char* const (&wb)
   int d = d_begin + wave;
   if (d >= d_end) return;
   u32x4 bv[NB][2];
-  float2 sc[NB];   // the two group scales of a double step (so[t] is even)
+  float2 sc[NB];   // the two group scales of a double step
   u32x4 av[2][4];
   auto load_w = [&](int t, int m, int dd) {
 #pragma unroll
@@ -362,7 +362,8 @@ MOE_DEV void stream_dsteps_i4_roll(const uint16_t* arow, const char* const (&wb)
       bv[t * NM + m][h] = ld16_nt(wb[m] + (wo[t][h] + (uint32_t)dd * 128u));
   };
   auto load_s = [&](int t, int m, int dd) {
-    sc[t * NM + m] = *reinterpret_cast<const float2*>(sb[m] + so[t] + 2u * (uint32_t)dd);
+    const float* p = sb[m] + so[t] + 2u * (uint32_t)dd;   // scale arrays are only 4-byte aligned
+    sc[t * NM + m] = make_float2(p[0], p[1]);
   };
   auto load_a = [&](int dd) {
 #pragma unroll
