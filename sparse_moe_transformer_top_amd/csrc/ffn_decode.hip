@@ -13,16 +13,18 @@
 // kernel 1; 16 down rows and one k split for kernel 2); its waves take the
 // row's k steps round-robin, so at any time the waves of a work-group read
 // neighbouring pieces of the same rows, and each lane keeps several 16-byte
-// weight loads outstanding (InFlight). bf16 weights are read in 128-byte
-// double steps by nontemporal loads that each cover whole lines
-// (dstep_operands); int8 and int4 weights in 64-byte steps, whose two halves
-// of a line are read by neighbouring waves. (Measured on MI355X at the
-// Grok-1 shape: interleaved steps beat one contiguous k range per wave, and
-// nontemporal loads of half lines lose about a quarter of the bandwidth.) The products run
-// on v_mfma_f32_16x16x32_bf16 with the expert's rows as the 16-row A operand
-// (rows past n_e are zero). The waves' partial sums are added in wave order
-// through LDS. int8 weights are loaded 16 per lane (64 k per step) and
-// converted exactly to bf16; their row scales multiply the float32 sums.
+// weight loads outstanding (InFlight). Weights are read in 128-byte double
+// steps by nontemporal loads that each cover whole lines (dstep_operands);
+// int8 and int4 rows that do not split into double steps fall back to
+// 64-byte steps, whose two halves of a line are read by neighbouring waves.
+// (Measured on MI355X at the Grok-1 shape: interleaved steps beat one
+// contiguous k range per wave, and nontemporal loads of half lines lose
+// about a quarter of the bandwidth.) The products run on
+// v_mfma_f32_16x16x32_bf16 with the expert's rows as the 16-row A operand
+// (rows past n_e are zero, or for int4 a repeat of the last row; neither is
+// stored). The waves' partial sums are added in wave order through LDS.
+// int8 weights are loaded 16 per lane (64 k per step) and converted exactly
+// to bf16; their row scales multiply the float32 sums.
 //
 // The down projection is split over kDownSplit k ranges so that a work unit
 // (16 rows x F/kDownSplit) is small against the whole launch and the last
