@@ -40,8 +40,15 @@ namespace {
 
 constexpr int kWavesGateUp = 16;
 constexpr int kWavesDown = 8;
+// int4 gate/up: 4 waves and two work-groups per CU (each wave takes twice
+// the double steps of an 8-wave work-group, and one work-group fills its
+// pipeline while the other drains it): 0.285 -> 0.271 ms at the Grok-1
+// decode shape against 8 waves and one work-group per CU
 #ifndef MOE_I4_GU_WAVES
-#define MOE_I4_GU_WAVES 8
+#define MOE_I4_GU_WAVES 4
+#endif
+#ifndef MOE_I4_GU_MINWG
+#define MOE_I4_GU_MINWG 2
 #endif
 #ifndef MOE_I4_DN_WAVES
 #define MOE_I4_DN_WAVES 8
@@ -567,9 +574,10 @@ __global__ __launch_bounds__(DownWaves<WT>::N * 64) void down_decode_kernel(FfnA
 // for down (0.224 ms against 0.266 for one tile with four). With full-line
 // double steps (stream_dsteps_i4, when the scale-group count is even): one
 // double step in flight, gate/up 0.354 ms and down 0.185 ms; then four
-// tiles for gate/up (the kernel already runs one work-group per CU, so the
-// extra registers cost no occupancy) 0.326 ms; one tile was within noise,
-// two double steps in flight, or four tiles for down, were slower.
+// tiles for gate/up (the kernel then ran one 8-wave work-group per CU, so
+// the extra registers cost no occupancy) 0.326 ms; one tile was within
+// noise, two double steps in flight, or four tiles for down, were slower.
+// With the pipelined stream and 4-wave work-groups, three tiles equal four.
 #ifndef MOE_I4_GU_NT
 #define MOE_I4_GU_NT 2
 #endif
@@ -584,7 +592,7 @@ constexpr int kI4GateUpTilesFull = MOE_I4_GU_NT_FULL;   // full-line double step
 constexpr int kI4DownTiles = MOE_I4_DN_NT;
 
 template <int NT>
-__global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64) void gateup_decode_i4_kernel(FfnArgs a) {
+__global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64, MOE_I4_GU_MINWG) void gateup_decode_i4_kernel(FfnArgs a) {
   constexpr int kWaves = GateUpWaves<WT_I4>::N;
   static_assert(NT <= kWaves, "one wave per tile in the epilogue");
   __shared__ float red[kWaves][2 * NT][4][64];
