@@ -118,16 +118,48 @@ def top_k_softmax(l32: np.ndarray, l64: np.ndarray, k: int,
     # stable sort of the negated values: equal logits keep ascending index
     order = np.argsort(-l32, axis=1, kind="stable")
     idx = order[:, :k].astype(np.int32)
-    sel = np.take_along_axis(l64, order[:, :k], axis=1)
-    z = np.exp(sel - sel[:, :1])
-    w = z / z.sum(axis=1, keepdims=True)
+    return Routing(idx, _selected_softmax(l64, idx), _tie_flags(l64, order, k, tie_tol), l32, l64)
 
+
+def _selected_softmax(l64: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Softmax over the selected logits of each token, exp(l_j - l_slot0) /
+    sum_j' exp(l_j' - l_slot0) (the constant subtracted does not change it)."""
+    sel = np.take_along_axis(l64, np.asarray(idx, np.int64), axis=1)
+    z = np.exp(sel - sel[:, :1])
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def _tie_flags(l64: np.ndarray, order: np.ndarray, k: int, tie_tol: float) -> np.ndarray:
+    """A decisive float64 gap (ranks j, j+1 for j < k) below tie_tol * max(1, max|l|)."""
+    T, E = l64.shape
     ranked64 = np.take_along_axis(l64, order, axis=1)
     last = min(k, E - 1)
     gaps = ranked64[:, :last] - ranked64[:, 1:last + 1]
     scale = np.maximum(1.0, np.abs(l64).max(axis=1)) if E > 0 else 1.0
-    tie = (gaps < tie_tol * scale[:, None]).any(axis=1) if last > 0 else np.zeros(T, bool)
-    return Routing(idx, w, tie, l32, l64)
+    return (gaps < tie_tol * scale[:, None]).any(axis=1) if last > 0 else np.zeros(T, bool)
+
+
+def routing_with_indices(l32: np.ndarray, l64: np.ndarray, idx: np.ndarray,
+                         tie_tol: float = 1e-4) -> Routing:
+    """Routing whose expert choice is given (idx [T,k], distinct per token)
+    instead of taken by the top-k rule; the weights are the same softmax over
+    the given selection, the tie flags those of the top-k rule.
+
+    Where the top-k rule is decided by a gap within the tie tolerance, more
+    than one choice is correct; this evaluates the layer for another such
+    choice (made by an implementation that ordered the near-equal logits
+    differently)."""
+    idx = np.asarray(idx, np.int32)
+    T, E = l32.shape
+    k = idx.shape[1]
+    if idx.shape[0] != T or not 1 <= k <= E:
+        raise ValueError("idx must be [T,k] with 1 <= k <= E")
+    if T and (idx.min() < 0 or idx.max() >= E):
+        raise ValueError("expert index out of range")
+    if k > 1 and T and np.any(np.diff(np.sort(idx, axis=1), axis=1) == 0):
+        raise ValueError("a token selects one expert twice")
+    order = np.argsort(-l32, axis=1, kind="stable")
+    return Routing(idx, _selected_softmax(l64, idx), _tie_flags(l64, order, k, tie_tol), l32, l64)
 
 
 # --------------------------------------------------------------------------
@@ -258,18 +290,21 @@ def layer_forward(x: np.ndarray, act: str, wr: np.ndarray,
                   k: int = 2, capacity_factor=None,
                   sg=None, su=None, sd=None,
                   tokens: Optional[np.ndarray] = None,
-                  tie_tol: float = 1e-4) -> LayerResult:
+                  tie_tol: float = 1e-4, idx: Optional[np.ndarray] = None) -> LayerResult:
     """Whole-layer forward. Routing and dispatch run over all T tokens (the
     capacity decision depends on every earlier token); the expert FFN and the
     combine run only for `tokens` (all tokens when None).
 
     out[t] = sum over kept slots j of w[t,j] * expert_{idx[t,j]}(x[t]),
-    slot 0 first; a token whose slots were all dropped gets a zero row."""
+    slot 0 first; a token whose slots were all dropped gets a zero row.
+    idx: the experts chosen per token, when given (routing_with_indices);
+    otherwise the top-k rule chooses."""
     x64 = widen(x, act)
     T, H = x64.shape
     E = np.asarray(wr).shape[0]
     l32, l64 = router_logits(x64, wr)
-    routing = top_k_softmax(l32, l64, k, tie_tol)
+    routing = top_k_softmax(l32, l64, k, tie_tol) if idx is None else \
+        routing_with_indices(l32, l64, idx, tie_tol)
     disp = dispatch(routing.idx, E, capacity_factor)
 
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
@@ -332,7 +367,7 @@ class LayerGrads:
 def layer_backward(x: np.ndarray, act: str, wr: np.ndarray,
                    wg: Sequence, wu: Sequence, wd: Sequence, wdt: str,
                    dout: np.ndarray, k: int = 2, capacity_factor=None,
-                   tie_tol: float = 1e-4) -> LayerGrads:
+                   tie_tol: float = 1e-4, idx: Optional[np.ndarray] = None) -> LayerGrads:
     """Gradients of L = sum(dout * out) for the layer of layer_forward, in
     float64 on the stored values (routing decided as in layer_forward).
 
@@ -346,14 +381,16 @@ def layer_backward(x: np.ndarray, act: str, wr: np.ndarray,
       dx_t    += dg Wg_e + du Wu_e
     Softmax over the selected logits, w_j = exp(l_j) / sum_j' exp(l_j'):
       dl[t, idx[t,j]] = w_j (dw_j - sum_j' w_j' dw_j'), zero for unselected
-    Router, logits = x Wr^T:  dx_t += dl_t Wr,  dWr = dl^T x."""
+    Router, logits = x Wr^T:  dx_t += dl_t Wr,  dWr = dl^T x.
+    idx: the experts chosen per token, when given (as in layer_forward)."""
     x64 = widen(x, act)
     T, H = x64.shape
     wr64 = np.asarray(wr, np.float32).astype(np.float64)
     E = wr64.shape[0]
     d64 = np.asarray(dout, np.float64)
     l32, l64 = router_logits(x64, wr)
-    routing = top_k_softmax(l32, l64, k, tie_tol)
+    routing = top_k_softmax(l32, l64, k, tie_tol) if idx is None else \
+        routing_with_indices(l32, l64, idx, tie_tol)
     disp = dispatch(routing.idx, E, capacity_factor)
 
     F = widen(wg[0], wdt).shape[0]
@@ -405,12 +442,15 @@ class SampledGrads:
     tokens: np.ndarray   # sampled tokens
     dx: np.ndarray       # [len(tokens), H]
     entries: dict        # name -> (indices [n,3] (e, row, col), values [n])
+    dwr: Optional[np.ndarray] = None   # [E,H] router weight gradient (router_grad=True)
 
 
 def layer_backward_sampled(x: np.ndarray, act: str, wr: np.ndarray,
                            wg: Sequence, wu: Sequence, wd: Sequence, wdt: str,
                            dout: np.ndarray, k: int, capacity_factor, tokens: np.ndarray,
-                           entries: dict, tie_tol: float = 1e-4) -> SampledGrads:
+                           entries: dict, tie_tol: float = 1e-4,
+                           idx: Optional[np.ndarray] = None, router_grad: bool = False,
+                           progress=None) -> SampledGrads:
     """Selected outputs of layer_backward at sizes where the whole backward
     is too slow on the CPU: dx for `tokens`, and the weight-gradient entries
     entries[name] = [(e, i, j), ...] for name in dwg / dwu ([e][f][h]) and
@@ -419,13 +459,20 @@ def layer_backward_sampled(x: np.ndarray, act: str, wr: np.ndarray,
       dWg[e][f][h] = sum_r dg_r[f] x_r[h],  dWu[e][f][h] = sum_r du_r[f] x_r[h]
     with h_r[f], dg_r[f], du_r[f] from column f of W_gate / W_up / W_down,
     and dx_t as in layer_backward (the token's own slots and its logits).
-    Expert weights are read one expert at a time (wg[e] etc. may be lazy)."""
+    Expert weights are read one expert at a time (wg[e] etc. may be lazy).
+
+    router_grad=True also gives the whole router weight gradient dWr = dl^T x,
+    which needs dw[t,j] = dout_t . y_(t,j) for every kept slot: each expert's
+    output rows are then evaluated for all of its rows (the full forward).
+    idx: the experts chosen per token, when given (as in layer_forward).
+    progress: optional callable taking a message, called once per expert."""
     x64 = widen(x, act)
     T, H = x64.shape
     wr64 = np.asarray(wr, np.float32).astype(np.float64)
     E = wr64.shape[0]
     l32, l64 = router_logits(x64, wr)
-    routing = top_k_softmax(l32, l64, k, tie_tol)
+    routing = top_k_softmax(l32, l64, k, tie_tol) if idx is None else \
+        routing_with_indices(l32, l64, idx, tie_tol)
     disp = dispatch(routing.idx, E, capacity_factor)
     tokens = np.asarray(tokens, np.int64)
 
@@ -434,6 +481,7 @@ def layer_backward_sampled(x: np.ndarray, act: str, wr: np.ndarray,
 
     dx = np.zeros((len(tokens), H))
     dw_tok = np.zeros((len(tokens), k))
+    dw_all = np.zeros((T, k)) if router_grad else None
     vals = {n: np.zeros(len(v)) for n, v in entries.items()}
     for e in range(E):
         rows = range(int(disp.offsets[e]), int(disp.offsets[e + 1]))
@@ -441,14 +489,21 @@ def layer_backward_sampled(x: np.ndarray, act: str, wr: np.ndarray,
         mine = {n: [i for i, (ee, _, _) in enumerate(v) if ee == e] for n, v in entries.items()}
         tok_slots = [(p, j) for p, t in enumerate(tokens) for j in range(k)
                      if routing.idx[t, j] == e and disp.slot_row[t * k + j] >= 0]
-        if len(slots) == 0 or (not any(mine.values()) and not tok_slots):
+        if len(slots) == 0 or (not any(mine.values()) and not tok_slots and not router_grad):
             continue
+        if progress is not None:
+            progress(f"oracle backward: expert {e}, {len(slots)} rows")
         ts, js = slots // k, slots % k
         X = x64[ts]
         wts = routing.w[ts, js]
         D = np.stack([d64(t) for t in ts]) if len(ts) else np.zeros((0, H))
         dy = wts[:, None] * D
         Wg, Wu, Wd = widen(wg[e], wdt), widen(wu[e], wdt), widen(wd[e], wdt)
+        if router_grad:
+            # dw of every kept slot of this expert: dout_t . y, y = h Wd^T
+            y = (silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T
+            dw_all[ts, js] = np.sum(D * y, axis=1)
+            del y
         # entries: per-column quantities over all of the expert's rows
         for n, ids in mine.items():
             for i in ids:
@@ -461,21 +516,30 @@ def layer_backward_sampled(x: np.ndarray, act: str, wr: np.ndarray,
                     dh = dy @ Wd[:, a]
                     col = dh * u * silu_grad(g) if n == "dwg" else dh * silu(g)
                     vals[n][i] = np.sum(col * X[:, b])
-        # the sampled tokens' own slots: whole rows
-        for p, j in tok_slots:
-            t = int(tokens[p])
-            xr = x64[t]
-            g, u = Wg @ xr, Wu @ xr
-            y = Wd @ (silu(g) * u)
-            dw_tok[p, j] = float(d64(t) @ y)
-            dh = (routing.w[t, j] * d64(t)) @ Wd
-            dx[p] += (dh * u * silu_grad(g)) @ Wg + (dh * silu(g)) @ Wu
+        # the sampled tokens' own slots: whole rows, all of this expert's at once
+        if tok_slots:
+            ps = np.array([p for p, _ in tok_slots], np.int64)
+            jsl = np.array([j for _, j in tok_slots], np.int64)
+            tt = tokens[ps]
+            g, u = x64[tt] @ Wg.T, x64[tt] @ Wu.T
+            y = (silu(g) * u) @ Wd.T
+            Ds = np.stack([d64(t) for t in tt])
+            dw_tok[ps, jsl] = np.sum(Ds * y, axis=1)
+            dh = (routing.w[tt, jsl][:, None] * Ds) @ Wd
+            np.add.at(dx, ps, (dh * u * silu_grad(g)) @ Wg + (dh * silu(g)) @ Wu)
     for p, t in enumerate(tokens):
         w = routing.w[t]
         dsel = w * (dw_tok[p] - np.sum(w * dw_tok[p]))
         dx[p] += dsel @ wr64[routing.idx[t].astype(np.int64)]
     ent = {n: (np.asarray(v, np.int64).reshape(-1, 3), vals[n]) for n, v in entries.items()}
-    return SampledGrads(routing, disp, tokens, dx, ent)
+    dwr = None
+    if router_grad:
+        # softmax over the selected logits of every token, then dWr = dl^T x
+        dsel = routing.w * (dw_all - np.sum(routing.w * dw_all, axis=1, keepdims=True))
+        dl = np.zeros((T, E))
+        np.put_along_axis(dl, routing.idx.astype(np.int64), dsel, axis=1)
+        dwr = dl.T @ x64
+    return SampledGrads(routing, disp, tokens, dx, ent, dwr)
 
 
 # --------------------------------------------------------------------------
@@ -483,10 +547,11 @@ def layer_backward_sampled(x: np.ndarray, act: str, wr: np.ndarray,
 # --------------------------------------------------------------------------
 
 
-def expert_batch_size(global_batch: int, seq_len: int, num_experts: int = 8,
-                      top_k: int = 2) -> float:
-    """Mean assignments per expert, batch*seq*k/E (section "Tradeoffs")."""
-    return global_batch * seq_len * top_k / num_experts
+def mean_rows_per_expert(T: int, k: int, E: int) -> float:
+    """Rows an expert receives on average: the T*k assignments spread over E
+    experts (the expert batch sizes of section "Tradeoffs: when MoE wins and
+    when it doesn't", whose token count is batch * sequence length)."""
+    return T * k / E
 
 
 def expert_params(hidden: int, expert_dim: int) -> int:

@@ -193,10 +193,67 @@ def test_sampled_backward_equals_full(cf):
            "dwd": [(int(rng.integers(8)), int(rng.integers(32)), int(rng.integers(64)))
                    for _ in range(20)]}
     tokens = np.array([0, 7, 19, 49])
+    for router_grad in (False, True):
+        s = oracle.layer_backward_sampled(inp.x, "bf16", inp.wr, inp.wg, inp.wu, inp.wd, "bf16",
+                                          dout=d64, k=2, capacity_factor=cf, tokens=tokens,
+                                          entries=ent, router_grad=router_grad)
+        assert np.allclose(s.dx, g.dx[tokens], rtol=1e-12, atol=1e-12)
+        for n, full in (("dwg", g.dwg), ("dwu", g.dwu), ("dwd", g.dwd)):
+            ids, v = s.entries[n]
+            assert np.allclose(v, full[ids[:, 0], ids[:, 1], ids[:, 2]], rtol=1e-12, atol=1e-13)
+        if router_grad:
+            # the whole router weight gradient, every token's logits
+            assert np.max(np.abs(s.dwr - g.dwr)) <= 1e-12 * max(1.0, np.abs(g.dwr).max())
+        else:
+            assert s.dwr is None
+
+
+def _other_choice(routing, E, seed):
+    """Indices that differ from the top-k rule's for about a third of the
+    tokens: slot 1 takes the third-ranked expert, or the two slots swap."""
+    rng = np.random.default_rng(seed)
+    idx = routing.idx.copy()
+    order = np.argsort(-routing.l32, axis=1, kind="stable")
+    for t in range(idx.shape[0]):
+        r = rng.random()
+        if r < 0.2:
+            idx[t, 1] = order[t, 2]
+        elif r < 0.35:
+            idx[t] = idx[t, ::-1]
+    return idx
+
+
+@pytest.mark.parametrize("cf", [None, 0.75])
+def test_given_indices_match_autograd(cf):
+    # the layer on a routing that is not the top-k rule's (given indices):
+    # torch autograd through the torch forward with the same selection, and
+    # the sampled evaluation (whole router gradient) against the full one
+    cfg = _cfg(T=36, H=24, F=40, E=6, k=2, cf=cf, act="bf16", wdt="bf16", seed=8)
+    inp = synth.generate_host(cfg)
+    dout = _dout(cfg, seed=12)
+    l32, l64 = oracle.router_logits(oracle.widen(inp.x, "bf16"), inp.wr)
+    idx = _other_choice(oracle.top_k_softmax(l32, l64, 2), cfg.E, seed=3)
+    g = oracle.layer_backward(inp.x, "bf16", inp.wr, inp.wg, inp.wu, inp.wd, "bf16", dout,
+                              k=2, capacity_factor=cf, idx=idx)
+    assert np.array_equal(g.routing.idx, idx)
+    if cf is not None:
+        assert g.disp.dropped.any()
+    leaf = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    x = leaf(oracle.widen(inp.x, "bf16"))
+    wr = leaf(np.asarray(inp.wr, np.float64))
+    wg = leaf(np.stack([oracle.widen(w, "bf16") for w in inp.wg]))
+    wu = leaf(np.stack([oracle.widen(w, "bf16") for w in inp.wu]))
+    wd = leaf(np.stack([oracle.widen(w, "bf16") for w in inp.wd]))
+    slot_row = oracle.dispatch(idx, cfg.E, cf).slot_row
+    out = _torch_forward(x, wr, wg, wu, wd, torch.tensor(idx, dtype=torch.int64), slot_row, 2)
+    (torch.tensor(dout) * out).sum().backward()
+    for mine, ref in ((g.out, out.detach()), (g.dx, x.grad), (g.dwr, wr.grad),
+                      (g.dwg, wg.grad), (g.dwu, wu.grad), (g.dwd, wd.grad)):
+        ref = ref.numpy()
+        assert np.max(np.abs(mine - ref)) <= 1e-12 * max(1.0, np.abs(ref).max())
     s = oracle.layer_backward_sampled(inp.x, "bf16", inp.wr, inp.wg, inp.wu, inp.wd, "bf16",
-                                      dout=d64, k=2, capacity_factor=cf, tokens=tokens,
-                                      entries=ent)
-    assert np.allclose(s.dx, g.dx[tokens], rtol=1e-12, atol=1e-12)
-    for n, full in (("dwg", g.dwg), ("dwu", g.dwu), ("dwd", g.dwd)):
-        ids, v = s.entries[n]
-        assert np.allclose(v, full[ids[:, 0], ids[:, 1], ids[:, 2]], rtol=1e-12, atol=1e-13)
+                                      dout=dout, k=2, capacity_factor=cf,
+                                      tokens=np.array([1, 20, 35]), entries={}, idx=idx,
+                                      router_grad=True)
+    assert np.max(np.abs(s.dwr - g.dwr)) <= 1e-12 * max(1.0, np.abs(g.dwr).max())
+    assert np.allclose(s.dx, g.dx[[1, 20, 35]], rtol=1e-12, atol=1e-12)

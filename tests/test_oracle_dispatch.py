@@ -127,7 +127,7 @@ def test_page_sizes_golden():
     assert g["w_gate_up_in_out"][0] == [H, 2 * F]
     assert g["w_down_in_out"][0] == [F, H]
     for b, s, per in g["expert_batch"]:
-        assert oracle.expert_batch_size(b, s, E, k) == per
+        assert oracle.mean_rows_per_expert(b * s, k, E) == per
         # the dispatch's mean rows per expert equals the printed figure when
         # all b*s tokens route without a drop
         assert b * s * k // E == per

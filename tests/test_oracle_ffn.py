@@ -51,6 +51,30 @@ def test_dense_masked_brute_force(name):
         assert res.disp.dropped.sum() > 0
 
 
+def test_given_indices_dense_masked_brute_force():
+    # a routing that is not the top-k rule's: the dense-masked reference with
+    # weights from torch's softmax over the same selected logits
+    cfg = synth.get_config("p_cap").with_(T=96, capacity_factor=0.75)
+    inp = synth.generate_host(cfg)
+    x64 = oracle.widen(inp.x, cfg.act)
+    l32, l64 = oracle.router_logits(x64, inp.wr)
+    rng = np.random.default_rng(4)
+    idx = np.stack([rng.choice(cfg.E, 2, replace=False) for _ in range(cfg.T)]).astype(np.int32)
+    res = _layer(inp, cfg, idx=idx)
+    assert np.array_equal(res.routing.idx, idx) and res.disp.dropped.any()
+    w = torch.softmax(torch.gather(torch.from_numpy(l64), 1, torch.from_numpy(idx).long()),
+                      dim=1).numpy()
+    assert np.allclose(res.routing.w, w, rtol=0, atol=1e-15)
+    ref = _dense_masked_reference(inp, cfg, res)
+    assert np.max(np.abs(res.out - ref)) <= 1e-10 * max(1.0, np.abs(ref).max())
+    # the top-k rule's own indices reproduce the default routing exactly
+    own = _layer(inp, cfg)
+    again = _layer(inp, cfg, idx=own.routing.idx)
+    assert np.array_equal(again.routing.w, own.routing.w) and np.array_equal(again.out, own.out)
+    with pytest.raises(ValueError):
+        _layer(inp, cfg, idx=np.zeros((cfg.T, 2), np.int32))     # one expert twice
+
+
 def test_sampled_tokens_equal_full_rows():
     cfg = synth.get_config("p_cap")
     inp = synth.generate_host(cfg)
