@@ -47,9 +47,16 @@ constexpr int kWavesDown = 8;
 #ifndef MOE_I4_GU_WAVES
 #define MOE_I4_GU_WAVES 4
 #endif
-#ifndef MOE_I4_GU_MINWG
-#define MOE_I4_GU_MINWG 2
+#ifndef MOE_I4_GU_WG_PER_CU
+#define MOE_I4_GU_WG_PER_CU 2
 #endif
+// HIP reads the second __launch_bounds__ argument as a minimum number of
+// waves per SIMD (amdgpu_waves_per_eu), not of work-groups per CU: W-wave
+// work-groups, G per CU, are G * W / 4 waves on each of the CU's 4 SIMDs
+// (two 4-wave work-groups: 2 per SIMD, a budget of 256 VGPRs per wave)
+constexpr int kI4GuWavesPerSimd = MOE_I4_GU_WG_PER_CU * MOE_I4_GU_WAVES / 4;
+static_assert(MOE_I4_GU_WG_PER_CU * MOE_I4_GU_WAVES % 4 == 0 && kI4GuWavesPerSimd >= 1,
+              "int4 gate/up work-groups per CU must fill the 4 SIMDs evenly");
 #ifndef MOE_I4_DN_WAVES
 #define MOE_I4_DN_WAVES 8
 #endif
@@ -592,7 +599,7 @@ constexpr int kI4GateUpTilesFull = MOE_I4_GU_NT_FULL;   // full-line double step
 constexpr int kI4DownTiles = MOE_I4_DN_NT;
 
 template <int NT>
-__global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64, MOE_I4_GU_MINWG) void gateup_decode_i4_kernel(FfnArgs a) {
+__global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64, kI4GuWavesPerSimd) void gateup_decode_i4_kernel(FfnArgs a) {
   constexpr int kWaves = GateUpWaves<WT_I4>::N;
   static_assert(NT <= kWaves, "one wave per tile in the epilogue");
   __shared__ float red[kWaves][2 * NT][4][64];

@@ -17,6 +17,7 @@ from .gen import (  # noqa: F401
     grad_output,
     HostInputs,
     generate_host,
+    router_inputs,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
     quantize_int8_rows,

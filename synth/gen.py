@@ -117,14 +117,39 @@ def skew_direction(x_stored_f32: np.ndarray) -> np.ndarray:
     return (m / n).astype(np.float32) if n > 0 else np.zeros_like(m, np.float32)
 
 
+def _draw_router_inputs(rng, cfg: LayerConfig):
+    """The first two draws of a layer instance: x (stored form) and the router
+    weight before the skew."""
+    T, H, E = cfg.T, cfg.H, cfg.E
+    f32 = np.float32
+    x32 = rng.standard_normal((T, H), dtype=f32)
+    wr = (rng.standard_normal((E, H), dtype=f32) * f32(1.0 / np.sqrt(H))).astype(f32)
+    x = bf16_bits_from_f32(x32) if cfg.act == "bf16" else x32
+    return x, wr
+
+
+def _apply_skew(x, wr, cfg: LayerConfig):
+    if cfg.skew:
+        u = skew_direction(x_as_f32(x, cfg.act))
+        for e, a in enumerate(cfg.skew):
+            wr[e] = (wr[e] + np.float32(a) * u).astype(np.float32)
+    return wr
+
+
+def router_inputs(cfg: LayerConfig, seed: Optional[int] = None):
+    """x and the router weight (skew applied) exactly as generate_host draws
+    them, without drawing the expert weights."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
+    x, wr = _draw_router_inputs(rng, cfg)
+    return x, _apply_skew(x, wr, cfg)
+
+
 def generate_host(cfg: LayerConfig, seed: Optional[int] = None) -> HostInputs:
     """Draw one layer instance on the host (sizes up to a few hundred MB)."""
     rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
     T, H, F, E = cfg.T, cfg.H, cfg.F, cfg.E
     f32 = np.float32
-    x32 = rng.standard_normal((T, H), dtype=f32)
-    wr = (rng.standard_normal((E, H), dtype=f32) * f32(1.0 / np.sqrt(H))).astype(f32)
-    x = bf16_bits_from_f32(x32) if cfg.act == "bf16" else x32
+    x, wr = _draw_router_inputs(rng, cfg)
 
     wdt_np = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "i4": np.uint8}[cfg.wdt]
     half = 2 if cfg.wdt == "i4" else 1
@@ -150,11 +175,7 @@ def generate_host(cfg: LayerConfig, seed: Optional[int] = None) -> HostInputs:
         if cfg.wdt in ("i8", "i4"):
             sg[e], su[e], sd[e] = s0, s1, s2
 
-    if cfg.skew:
-        u = skew_direction(x_as_f32(x, cfg.act))
-        for e, a in enumerate(cfg.skew):
-            wr[e] = (wr[e] + f32(a) * u).astype(f32)
-
+    wr = _apply_skew(x, wr, cfg)
     return HostInputs(cfg, x, wr, wg, wu, wd, sg, su, sd)
 
 

@@ -45,3 +45,37 @@ def test_storage_dtypes():
         assert inp.wg.shape == (cfg.E, cfg.F, cfg.H) and inp.wd.shape == (cfg.E, cfg.H, cfg.F)
         if cfg.wdt == "i8":
             assert inp.sg.shape == (cfg.E, cfg.F) and inp.sd.shape == (cfg.E, cfg.H)
+
+
+def _top1_shares(cfg, skew=None):
+    import oracle
+    x, wr = synth.router_inputs(cfg if skew is None else cfg.with_(skew=skew))
+    l32, l64 = oracle.router_logits(oracle.widen(x, cfg.act), wr)
+    return np.bincount(oracle.top_k_softmax(l32, l64, cfg.k).idx[:, 0], minlength=cfg.E) / cfg.T
+
+
+def test_router_inputs_are_generate_hosts_draws():
+    cfg = synth.get_config("p_skew")
+    a = synth.generate_host(cfg)
+    x, wr = synth.router_inputs(cfg)
+    assert np.array_equal(a.x, x) and np.array_equal(a.wr, wr)
+
+
+def test_skew_magnitudes_give_the_target_top1_shares():
+    # The skewed workloads ask for about 50% / 25% of the top-1 picks on
+    # experts 0 / 1; the stored magnitudes (along the mean direction of x)
+    # were chosen on a 0.2 grid with the host draws of seed 0. At T = 4096
+    # they reach the target within a percent and no neighbour on the grid is
+    # closer; at T = 16384 the stored pair gives the closest shares the grid
+    # reached (the second expert's share falls as the first's rises).
+    cfg = synth.CONFIGS["skew"]
+    a0, a1 = cfg.skew
+    s = _top1_shares(cfg)
+    assert abs(s[0] - 0.50) < 0.01 and abs(s[1] - 0.25) < 0.01, s[:2]
+    dist = lambda v: (v[0] - 0.5) ** 2 + (v[1] - 0.25) ** 2
+    for d0 in (-0.2, 0.0, 0.2):
+        for d1 in (-0.2, 0.0, 0.2):
+            if d0 or d1:
+                assert dist(_top1_shares(cfg, (a0 + d0, a1 + d1))) >= dist(s) - 1e-12
+    big = _top1_shares(synth.CONFIGS["capacity"])
+    assert 0.46 < big[0] < 0.48 and 0.22 < big[1] < 0.23, big[:2]
