@@ -82,6 +82,37 @@ def check_routing(idx_gpu: np.ndarray, w_gpu: np.ndarray, routing: "oracle.Routi
     return diff
 
 
+def check_topk_valid(idx_gpu: np.ndarray, routing: "oracle.Routing", tie_tol: float = 1e-4):
+    """Every token's selection is a correct top-k choice: the expert in slot j
+    has the j-th largest float64 logit up to the tie tolerance (where near-
+    equal logits make several choices correct, any of them passes)."""
+    k = idx_gpu.shape[1]
+    l64 = routing.l64
+    ranked = -np.sort(-l64, axis=1)[:, :k]
+    sel = np.take_along_axis(l64, idx_gpu.astype(np.int64), axis=1)
+    scale = np.maximum(1.0, np.abs(l64).max(axis=1, keepdims=True))
+    bad = np.abs(sel - ranked) > k * tie_tol * scale
+    assert not bad.any(), f"{int(bad.any(axis=1).sum())} tokens with an invalid top-k choice"
+
+
+def gpu_routing(idx_gpu: np.ndarray, w_gpu: np.ndarray, routing: "oracle.Routing"):
+    """Checks the GPU's routing against the oracle's (check_routing, then the
+    validity of every choice) and returns the indices the reference must use:
+    None when they are the oracle's own, else the GPU's (differing only on
+    tie-flagged tokens, where both choices are correct)."""
+    diff = check_routing(idx_gpu, w_gpu, routing)
+    check_topk_valid(idx_gpu, routing)
+    if diff.any():
+        log(f"  {int(diff.sum())} tie-flagged tokens ordered differently: reference on the "
+            "GPU's own choice")
+        return idx_gpu
+    return None
+
+
+def check_weights(w_gpu: np.ndarray, routing: "oracle.Routing"):
+    assert np.max(np.abs(w_gpu - routing.w)) <= W_ATOL
+
+
 def check_dispatch_equal(got: dict, ref: "oracle.Dispatch"):
     assert np.array_equal(got["counts"], ref.counts)
     assert np.array_equal(got["offsets"], ref.offsets)

@@ -14,7 +14,8 @@ import torch
 import oracle
 import synth
 from synth.device import generate_device
-from gpu_helpers import LazyExperts, check_close, check_routing, host_array, log, out_as_f64
+from gpu_helpers import (LazyExperts, check_close, check_dispatch_equal, check_weights,
+                         gpu_routing, host_array, log, out_as_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +31,14 @@ def moe():
     torch.cuda.empty_cache()
 
 
+# medium batches at the Grok-1 H and F (the page's batch = 1, seq = 512 point
+# and two smaller ones): 16 to 128 rows per expert
+MEDIUM = {f"t{T}": synth.CONFIGS["medium"].with_(name=f"t{T}", T=T, seed=70 + T)
+          for T in (64, 128)}
+
+
 def inputs(name):
-    cfg = synth.CONFIGS[name]
+    cfg = synth.CONFIGS[name] if name in synth.CONFIGS else MEDIUM[name]
     # bf16 workloads share one weight set (same seed): draw it once
     if cfg.wdt == "bf16":
         if "bf16" not in _weights:
@@ -46,7 +53,8 @@ def inputs(name):
     return cfg, generate_device(cfg, "cuda")
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "capacity", "decode_i4"])
+@pytest.mark.parametrize("name", ["decode", "t64", "t128", "medium", "prefill", "skew",
+                                  "capacity", "decode_i4"])
 def test_fullsize_layer(moe, name):
     cfg, d = inputs(name)
     _check_layer(moe, cfg, d, name)
@@ -78,28 +86,33 @@ def _check_layer(moe, cfg, d, name):
         np.random.default_rng(1).choice(T, 256, replace=False))
     sc = {n: (None if getattr(d, n) is None else host_array(getattr(d, n)))
           for n in ("sg", "su", "sd")}
-    log(f"  oracle on {len(sample)} tokens")
-    res = oracle.layer_forward(host_array(d.x), cfg.act, host_array(d.wr), LazyExperts(d.wg),
-                               LazyExperts(d.wu), LazyExperts(d.wd), cfg.wdt, k=cfg.k,
+    x_h, wr_h = host_array(d.x), host_array(d.wr)
+    # routing of every token against the oracle's; the reference then uses
+    # the GPU's own choice where a tie-flagged token was ordered differently
+    l32, l64 = oracle.router_logits(oracle.widen(x_h, cfg.act), wr_h)
+    routing = oracle.top_k_softmax(l32, l64, cfg.k)
+    idx, w = host_array(ax["topk_idx"]), host_array(ax["topk_w"])
+    own = gpu_routing(idx, w, routing)
+    log(f"  tie-flagged tokens {int(routing.tie.sum())}; oracle on {len(sample)} tokens")
+    res = oracle.layer_forward(x_h, cfg.act, wr_h, LazyExperts(d.wg), LazyExperts(d.wu),
+                               LazyExperts(d.wd), cfg.wdt, k=cfg.k,
                                capacity_factor=cfg.capacity_factor, sg=sc["sg"], su=sc["su"],
-                               sd=sc["sd"], tokens=sample)
-    idx = host_array(ax["topk_idx"])
-    diff = check_routing(idx, host_array(ax["topk_w"]), res.routing)
-    log(f"  tie-flagged tokens {int(res.routing.tie.sum())}, differing {int(diff.sum())}")
-    if not diff.any():
-        assert np.array_equal(host_array(ax["counts"]), res.disp.counts)
-        assert np.array_equal(host_array(ax["offsets"]), res.disp.offsets)
-        assert np.array_equal(host_array(ax["dropped"]), res.disp.dropped)
-        keep = np.ones(len(sample), bool)
-    else:
-        assert cfg.capacity_factor is None, "tie flip under capacity: compare by hand"
-        keep = ~diff[sample]
-    got = out_as_f64(out)[sample]
-    r = check_close(got[keep], res.out[keep], cfg.act, f"{name} out")
+                               sd=sc["sd"], tokens=sample, idx=own)
+    check_weights(w, res.routing)
+    # dispatch of all T*k assignments, bit-exact: the layer's counts, offsets
+    # and drops, and perm / slot_row of the dispatch of the layer's indices
+    assert np.array_equal(host_array(ax["counts"]), res.disp.counts)
+    assert np.array_equal(host_array(ax["offsets"]), res.disp.offsets)
+    assert np.array_equal(host_array(ax["dropped"]), res.disp.dropped)
+    got = moe.moe_dispatch(ax["topk_idx"], cfg.E, cfg.capacity_factor)
+    torch.cuda.synchronize()
+    check_dispatch_equal({k: host_array(v) for k, v in got.items()}, res.disp)
+    r = check_close(out_as_f64(out)[sample], res.out, cfg.act, f"{name} out")
     log(f"  out: max ratio {r[0]:.2e}, l2 ratio {r[1]:.2e}")
     if cfg.capacity_factor is not None:
         assert res.disp.cap == 5120
-        assert int(host_array(ax["dropped"]).sum()) > 0
+        assert int(res.disp.dropped.sum()) > 0
+        log(f"  kept {int(res.disp.offsets[-1])} of {T * cfg.k} assignments")
     if cfg.skew:
         top1 = np.bincount(idx[:, 0], minlength=cfg.E) / T
         log(f"  top-1 shares {np.round(top1, 3).tolist()}")

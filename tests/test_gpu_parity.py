@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import (check_close, check_dispatch_equal, check_routing, dev_tensor,
-                         host_array, log, out_as_f64, to_device)
+from gpu_helpers import (check_close, check_dispatch_equal, check_routing, check_weights,
+                         dev_tensor, gpu_routing, host_array, log, out_as_f64, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -143,22 +143,24 @@ def test_layer_forward(moe, name):
                                     capacity_factor=cfg.capacity_factor, s_gate=d["sg"],
                                     s_up=d["su"], s_down=d["sd"], aux=True)
     torch.cuda.synchronize()
-    idx = host_array(ax["topk_idx"])
-    diff = check_routing(idx, host_array(ax["topk_w"]), res.routing)
-    got = dict(counts=host_array(ax["counts"]), offsets=host_array(ax["offsets"]),
-               dropped=host_array(ax["dropped"]))
-    if not diff.any():
-        assert np.array_equal(got["counts"], res.disp.counts)
-        assert np.array_equal(got["offsets"], res.disp.offsets)
-        assert np.array_equal(got["dropped"], res.disp.dropped)
-        check_close(out_as_f64(out), res.out, cfg.act, "out")
-    else:
-        # a tie flipped: compare the tokens it cannot affect (no capacity)
-        assert cfg.capacity_factor is None, "tie flip under capacity: compare by hand"
-        keep = ~diff
-        check_close(out_as_f64(out)[keep], res.out[keep], cfg.act, "out (non-tie)")
+    w = host_array(ax["topk_w"])
+    own = gpu_routing(host_array(ax["topk_idx"]), w, res.routing)
+    if own is not None:
+        res = oracle.layer_forward(inp.x, cfg.act, inp.wr, inp.wg, inp.wu, inp.wd, cfg.wdt,
+                                   k=cfg.k, capacity_factor=cfg.capacity_factor, sg=inp.sg,
+                                   su=inp.su, sd=inp.sd, idx=own)
+    check_weights(w, res.routing)
+    # the layer's dispatch outputs, and the dispatch of the layer's own indices
+    # (perm, slot_row), bit-exact against the oracle's dispatch of the same indices
+    assert np.array_equal(host_array(ax["counts"]), res.disp.counts)
+    assert np.array_equal(host_array(ax["offsets"]), res.disp.offsets)
+    assert np.array_equal(host_array(ax["dropped"]), res.disp.dropped)
+    got = moe.moe_dispatch(ax["topk_idx"], cfg.E, cfg.capacity_factor)
+    torch.cuda.synchronize()
+    check_dispatch_equal({k: host_array(v) for k, v in got.items()}, res.disp)
+    check_close(out_as_f64(out), res.out, cfg.act, "out")
     if cfg.capacity_factor is not None:
-        assert got["dropped"].sum() > 0
+        assert res.disp.dropped.sum() > 0
 
 
 def test_layer_determinism(moe):
