@@ -303,6 +303,39 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
                              void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The layer forward without any allocation, for callers that cannot call
+ * hipMalloc or take a caller-owned workspace: code under HIP graph capture,
+ * tight serving (decode) loops, harnesses that forbid allocation.
+ *
+ * Same arguments, checks, kernels and results as moe_layer_forward (bitwise),
+ * minus ws / ws_bytes: the workspace is a fixed device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB), one per GPU, present from the moment
+ * the library's device code is loaded on that GPU until the process ends.
+ * Calls whose moe_layer_workspace_bytes(...) exceeds that size return
+ * MOE_ERR_UNSUPPORTED and enqueue nothing (at the Grok-1 shape, H = 6144 and
+ * F = 32768, the decode sizes T <= 16 fit: about 8.4 MiB at T = 16; larger T
+ * take the tiled path, whose workspace is hundreds of MiB).
+ *
+ * The first call on a device looks up the array's address on that device
+ * (hipGetSymbolAddress, no stream operation); later calls only read it. The
+ * call allocates and frees nothing, and no part of the array needs to start
+ * at zero (every call writes what it later reads).
+ * Every call on one GPU shares that GPU's array and leaves the last call's
+ * contents in it: calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race and give undefined results; use
+ * moe_layer_forward with workspaces of their own for that.
+ * ------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+moe_status moe_layer_forward_noalloc(const void* x, moe_dtype act_dtype, const float* w_router,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     moe_dtype w_dtype,
+                                     const float* s_gate, const float* s_up, const float* s_down,
+                                     int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                                     float capacity_factor, void* out,
+                                     int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                     int32_t* offsets, uint8_t* dropped, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Training: a forward that keeps what the backward needs, and the backward.
  * The page gives the forward (GrokMoELayer.forward) and applies the capacity
  * drop in training (grok_router_forward and the paragraph after it); the

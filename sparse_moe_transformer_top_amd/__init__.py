@@ -19,10 +19,11 @@ from .api import (  # noqa: F401
     moe_layer_backward,
     moe_layer_backward_weights,
     moe_layer_forward,
+    moe_layer_forward_noalloc,
     moe_layer_forward_train,
     moe_router_topk,
     moe_routing_stats,
     train_reserve_bytes,
     train_reserve_views,
 )
-from ._lib import MoeError, LIB_PATH, load as load_library  # noqa: F401
+from ._lib import MoeError, LIB_PATH, NOALLOC_SCRATCH_BYTES, load as load_library  # noqa: F401

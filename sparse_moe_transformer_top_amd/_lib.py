@@ -22,6 +22,9 @@ MOE_ERR_HIP = 4
 
 MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
 
+# MOE_NOALLOC_SCRATCH_BYTES: the fixed workspace of moe_layer_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
 # exported symbols and their (restype, argtypes)
 _P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 SIGNATURES = {
@@ -45,6 +48,9 @@ SIGNATURES = {
     "moe_layer_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, C.c_int, C.c_int]),
     "moe_layer_forward": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _P, _P, _P, _I64, _I32,
                                     _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_noalloc": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _P, _P, _P,
+                                            _I64, _I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P,
+                                            _P, _P]),
     "moe_layer_train_reserve_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "moe_layer_backward_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "moe_layer_forward_train": (C.c_int, [_P, C.c_int, _P, _P, _P, _P, C.c_int, _I64, _I32, _I32,

@@ -238,6 +238,34 @@ def moe_layer_forward(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Ten
     return (out, ax) if aux else out
 
 
+def moe_layer_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor, w_gate: torch.Tensor,
+                              w_up: torch.Tensor, w_down: torch.Tensor, k: int = 2,
+                              capacity_factor: Optional[float] = None, s_gate=None, s_up=None,
+                              s_down=None, out: Optional[torch.Tensor] = None,
+                              aux: Optional[dict] = None):
+    """moe_layer_forward on the library's fixed scratch array instead of a
+    workspace (no allocation by the library; shapes whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES are rejected). out and the aux buffers (topk_idx,
+    topk_w, counts, offsets, dropped, each optional) are the caller's, so a
+    call with them given allocates nothing. Returns out."""
+    _need(x, "x", (torch.float32, torch.bfloat16), 2)
+    _need(w_router, "w_router", torch.float32, 2)
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, n, _WDT, 3)
+    T, H = x.shape
+    E, F, _ = w_gate.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, 2)
+    ax = aux or {}
+    g = (lambda n: _p(ax.get(n)))
+    check(_lib.load().moe_layer_forward_noalloc(
+        _p(x), _DT[x.dtype], _p(w_router), _p(w_gate), _p(w_up), _p(w_down), _DT[w_gate.dtype],
+        _p(s_gate), _p(s_up), _p(s_down), T, H, F, E, k, _cf(capacity_factor), _p(out),
+        g("topk_idx"), g("topk_w"), g("counts"), g("offsets"), g("dropped"), _stream(x.device)))
+    return out
+
+
 def train_reserve_bytes(T: int, H: int, F: int, E: int, k: int) -> int:
     return _lib.load().moe_layer_train_reserve_bytes(T, H, F, E, k)
 

@@ -531,25 +531,22 @@ size_t moe_layer_workspace_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int
   return layer_ws_layout(nullptr, T, H, F, E, k, act_dtype, w_dtype).total;
 }
 
-moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_router,
-                             const void* w_gate, const void* w_up, const void* w_down,
-                             moe_dtype w_dtype, const float* s_gate, const float* s_up,
-                             const float* s_down, int64_t T, int32_t H, int32_t F, int32_t E,
-                             int32_t k, float capacity_factor, void* out, int32_t* topk_idx,
-                             float* topk_w, int32_t* counts, int32_t* offsets, uint8_t* dropped,
-                             void* ws, size_t ws_bytes, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer forward's argument checks (everything but the workspace).
+moe_status check_layer(const void* x, moe_dtype act_dtype, const float* w_router,
+                       const void* w_gate, const void* w_up, const void* w_down,
+                       moe_dtype w_dtype, const float* s_gate, const float* s_up,
+                       const float* s_down, int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
+                       float capacity_factor, const void* out) {
   moe_status st;
   if ((st = check_shape(T, E, k)) || (st = check_dim("H", H)) || (st = check_dim("F", F)) ||
       (st = check_pair(act_dtype, w_dtype)) || (st = check_int4(T, H, F, w_dtype)))
     return st;
   REQUIRE(!std::isnan(capacity_factor), MOE_ERR_INVALID_ARGUMENT, "capacity_factor is NaN");
-  if (T == 0) {
-    // nothing to compute; the optional per-expert outputs are zeros
-    hipError_t e = hipSuccess;
-    if (counts) e = launch_fill_i32(counts, E, 0, (hipStream_t)stream);
-    if (e == hipSuccess && offsets) e = launch_fill_i32(offsets, E + 1, 0, (hipStream_t)stream);
-    return hip_status(e, "layer (empty input)");
-  }
+  if (T == 0) return ok();
   REQUIRE(x && w_router && w_gate && w_up && w_down && out, MOE_ERR_INVALID_ARGUMENT,
           "x, w_router, w_gate, w_up, w_down and out must be non-NULL");
   const bool i8 = has_scales(w_dtype);
@@ -559,11 +556,24 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
   REQUIRE(aligned16(x) && aligned16(w_router) && aligned16(w_gate) && aligned16(w_up) &&
               aligned16(w_down) && aligned16(out),
           MOE_ERR_INVALID_ARGUMENT, "x, weights and out must be 16-byte aligned");
-  REQUIRE(!std::isnan(capacity_factor), MOE_ERR_INVALID_ARGUMENT, "capacity_factor is NaN");
-  const LayerWs need = layer_ws_layout(nullptr, T, H, F, E, k, act_dtype, w_dtype);
-  REQUIRE(ws && ws_bytes >= need.total && aligned16(ws), MOE_ERR_WORKSPACE_TOO_SMALL,
-          "layer workspace: need %zu bytes (16-byte aligned), got %zu", need.total,
-          ws ? ws_bytes : (size_t)0);
+  return ok();
+}
+
+// The layer forward's launches, on a checked workspace of the layer's size.
+moe_status run_layer(const void* x, moe_dtype act_dtype, const float* w_router,
+                     const void* w_gate, const void* w_up, const void* w_down, moe_dtype w_dtype,
+                     const float* s_gate, const float* s_up, const float* s_down, int64_t T,
+                     int32_t H, int32_t F, int32_t E, int32_t k, float capacity_factor, void* out,
+                     int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                     uint8_t* dropped, void* ws, moe_stream_t stream) {
+  moe_status st;
+  if (T == 0) {
+    // nothing to compute; the optional per-expert outputs are zeros
+    hipError_t e = hipSuccess;
+    if (counts) e = launch_fill_i32(counts, E, 0, (hipStream_t)stream);
+    if (e == hipSuccess && offsets) e = launch_fill_i32(offsets, E + 1, 0, (hipStream_t)stream);
+    return hip_status(e, "layer (empty input)");
+  }
   hipStream_t s = (hipStream_t)stream;
   LayerWs L = layer_ws_layout(static_cast<char*>(ws), T, H, F, E, k, act_dtype, w_dtype);
   int32_t* idx = topk_idx ? topk_idx : L.idx;
@@ -581,6 +591,58 @@ moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_
                s_up, s_down, L.h, L.y, L.fws, s);
   if (st) return st;
   return hip_status(launch_combine(L.y, L.slot_row, w, T, H, k, act, out, s), "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward(const void* x, moe_dtype act_dtype, const float* w_router,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             moe_dtype w_dtype, const float* s_gate, const float* s_up,
+                             const float* s_down, int64_t T, int32_t H, int32_t F, int32_t E,
+                             int32_t k, float capacity_factor, void* out, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets, uint8_t* dropped,
+                             void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_layer(x, act_dtype, w_router, w_gate, w_up, w_down, w_dtype, s_gate, s_up,
+                        s_down, T, H, F, E, k, capacity_factor, out)))
+    return st;
+  if (T > 0) {
+    const size_t need = layer_ws_layout(nullptr, T, H, F, E, k, act_dtype, w_dtype).total;
+    REQUIRE(ws && ws_bytes >= need && aligned16(ws), MOE_ERR_WORKSPACE_TOO_SMALL,
+            "layer workspace: need %zu bytes (16-byte aligned), got %zu", need,
+            ws ? ws_bytes : (size_t)0);
+  }
+  return run_layer(x, act_dtype, w_router, w_gate, w_up, w_down, w_dtype, s_gate, s_up, s_down,
+                   T, H, F, E, k, capacity_factor, out, topk_idx, topk_w, counts, offsets,
+                   dropped, ws, stream);
+}
+
+moe_status moe_layer_forward_noalloc(const void* x, moe_dtype act_dtype, const float* w_router,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     moe_dtype w_dtype, const float* s_gate, const float* s_up,
+                                     const float* s_down, int64_t T, int32_t H, int32_t F,
+                                     int32_t E, int32_t k, float capacity_factor, void* out,
+                                     int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                     int32_t* offsets, uint8_t* dropped, moe_stream_t stream) {
+  moe_status st;
+  if ((st = check_layer(x, act_dtype, w_router, w_gate, w_up, w_down, w_dtype, s_gate, s_up,
+                        s_down, T, H, F, E, k, capacity_factor, out)))
+    return st;
+  void* ws = nullptr;
+  if (T > 0) {
+    const size_t need = layer_ws_layout(nullptr, T, H, F, E, k, act_dtype, w_dtype).total;
+    REQUIRE(need <= MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED,
+            "moe_layer_forward_noalloc: this shape needs %zu bytes of workspace, above the "
+            "library's fixed %zu (use moe_layer_forward with a workspace)",
+            need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    const hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "moe_layer_forward_noalloc: scratch lookup");
+  }
+  return run_layer(x, act_dtype, w_router, w_gate, w_up, w_down, w_dtype, s_gate, s_up, s_down,
+                   T, H, F, E, k, capacity_factor, out, topk_idx, topk_w, counts, offsets,
+                   dropped, ws, stream);
 }
 
 size_t moe_layer_train_reserve_bytes(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k) {

@@ -105,6 +105,10 @@ size_t decode_ws_bytes(int64_t T, int H, int k);
 hipError_t launch_gateup_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s);
 
+// noalloc.hip: device address of the library's fixed scratch array
+// (MOE_NOALLOC_SCRATCH_BYTES) on the current device, looked up once per device
+hipError_t noalloc_scratch(void** ptr);
+
 // routing statistics (stats.hip)
 hipError_t launch_routing_stats(const float* logits, const int32_t* counts, int64_t T, int E,
                                 int k, float* util, float* margin, float* mass, hipStream_t s);

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -186,6 +186,37 @@ def test_layer_argument_errors(lib):
     assert layer(lib, cf=math.nan) == INV
     assert layer(lib, act=F32, wdt=I8, scales=(P, P, P)) == UNS
     assert layer(lib, k=3, E=2) == INV
+
+
+def layer_noalloc(lib, T=16, H=6144, F=32768, E=8, k=2, act=BF16, wdt=BF16, cf=0.0,
+                  scales=(None, None, None), out=P, x=P):
+    return lib.moe_layer_forward_noalloc(x, act, P, P, P, P, wdt, *scales, T, H, F, E, k, cf, out,
+                                         None, None, None, None, None, None)
+
+
+def test_layer_noalloc_argument_errors(lib):
+    # every check runs before the scratch lookup and any launch
+    assert layer_noalloc(lib, out=None) == INV
+    assert layer_noalloc(lib, x=MIS) == INV
+    assert layer_noalloc(lib, cf=math.nan) == INV
+    assert layer_noalloc(lib, act=F32, wdt=I8, scales=(P, P, P)) == UNS
+    # a workspace above the fixed scratch: rejected, nothing enqueued
+    n = lib.moe_layer_workspace_bytes(17, 6144, 32768, 8, 2, BF16, BF16)
+    assert n > _lib.NOALLOC_SCRATCH_BYTES
+    assert layer_noalloc(lib, T=17) == UNS
+    assert "workspace" in lib.moe_last_error().decode()
+    # the Grok-1 decode sizes fit the scratch
+    for T in (1, 8, 16):
+        for wdt, sc in ((BF16, (None, None, None)), (I8, (P, P, P)), (I4, (P, P, P))):
+            assert lib.moe_layer_workspace_bytes(T, 6144, 32768, 8, 2, BF16, wdt) <= \
+                _lib.NOALLOC_SCRATCH_BYTES
+    assert layer_noalloc(lib, T=0) == OK      # empty input with no optional outputs: no launch
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_sizes(lib):
