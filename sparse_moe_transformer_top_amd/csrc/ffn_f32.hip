@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(FfnArgs a, uint32_t n_ntil
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[NB][BK][BN + 4];
   GroupedTile tile;
-  if (!grouped_tile(a.offsets, a.E, BM, n_ntiles, blockIdx.x, tile)) return;
+  if (!grouped_tile(a.offsets, a.E, BM, n_ntiles, kClsAll, blockIdx.x, tile)) return;
   const int N = GATEUP ? a.F : a.H;
   const int K = GATEUP ? a.H : a.F;
   const int n0 = tile.nt * BN;

@@ -12,10 +12,15 @@
 // [n][k]), so each 16-byte load holds 8 consecutive k of one row, which is the
 // per-lane operand of v_mfma_f32_32x32x16_bf16.
 //
-// A work-group of 8 waves computes a tile of
-// 256 activation rows x 256 weight rows (gate 128 + up 128, or 256 down
-// columns); waves form a 4 x 2 grid, each wave 64 rows x 4 weight sub-tiles
-// of 32 (8 MFMA accumulators of 32x32, two waves per SIMD). k advances in
+// A work-group of 8 waves computes a tile of activation rows x weight rows,
+// of one of two shapes chosen per expert by its row count (from the dispatch
+// offsets, on the device): the wide tiles, 256 rows x 256 weight rows (gate
+// 128 + up 128, or 256 down columns), waves in a 4 x 2 grid, for experts with
+// more than 128 rows; the stream tiles, 128 rows x 512 weight rows, waves in
+// a 2 x 4 grid, for experts with at most 128 rows (medium batches), whose
+// weights stream once from HBM while the few activation rows are re-read from
+// L2 per column tile, so a wider tile means fewer re-reads. Either way each
+// wave holds 8 MFMA accumulators of 32x32 (two waves per SIMD). k advances in
 // slices of 64 through a two-stage LDS ring filled by direct global->LDS
 // loads (global_load_lds_dwordx4, no register staging); the activation rows
 // of the gate/up product are gathered from x through the dispatch permutation
@@ -39,15 +44,18 @@ namespace {
 // direct-to-LDS pipelined grouped GEMM
 // ---------------------------------------------------------------------------
 constexpr int MBM = 256;   // activation rows per tile
-constexpr int MNB = 256;   // weight rows per tile
+constexpr int MNB = 256;   // weight rows per tile of the wide tiles (the stream tiles: 128)
 constexpr int MBK = 64;    // k per LDS stage
 constexpr int MNW = 8;                             // waves per work-group
 constexpr int MLPW = MBM * 8 / 64 / MNW;           // A LDS-DMA loads per wave per stage
-// wave grid (rows x weight rows): 4 x 2 for bf16 weights; 2 x 4 for int8, so
-// that each converted int8 operand is shared by fewer waves (the conversion
-// runs on the VALU once per wave that uses the operand)
-template <int WT> struct WaveGrid { static constexpr int M = 4, N = 2; };
-template <> struct WaveGrid<WT_I8> { static constexpr int M = 2, N = 4; };
+// wave grid (rows x weight rows): 4 x 2 on the wide bf16 tiles; 2 x 4 on the
+// stream tiles (128 rows) and with int8 weights, where each converted int8
+// operand is then shared by fewer waves (the conversion runs on the VALU once
+// per wave that uses the operand)
+template <int WT, int BM, int BN> struct WaveGrid {
+  static constexpr int M = BM == 256 && !(WT == WT_I8) ? 4 : 2;
+  static constexpr int N = MNW / M;
+};
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -99,43 +107,57 @@ MOE_DEV void block_sync() {
 // pre-activations g and u (bf16), which the backward reads.
 enum Mode { M_DOWN = 0, M_GATEUP = 1, M_GATEUP_SAVE = 2 };
 
-template <int WT> struct BTile {
+template <int WT, int BN> struct BTile {
   static constexpr int ESZ = WT == WT_I8 ? 1 : 2;       // weight element bytes
   static constexpr int BCH = MBK * ESZ / 16;            // 16-byte chunks per B row
-  static constexpr int LPW = MNB * BCH / 64 / MNW;      // B LDS-DMA loads per wave per stage
+  static constexpr int LPW = BN * BCH / 64 / MNW;       // B LDS-DMA loads per wave per stage
 };
+
+// s_waitcnt until this wave's loads of the stage being waited for have
+// landed while those of `later` (0 .. 2) later stages may still be in flight
+// (LPS loads per stage).
+template <int LPS>
+MOE_DEV void wait_landed(int later) {
+  if (later >= 2) wait_vmcnt<2 * LPS>();
+  else if (later == 1) wait_vmcnt<LPS>();
+  else wait_vmcnt<0>();
+}
 
 // The pipelined k loop, shared by the kernels of this file as macros over
 // the kernel's own locals (a device function here changed the forward
-// kernel's instruction schedule): KT >= 1 stages of MBK through the
-// two-stage LDS ring SA/SB (sT0, sT1 hold the A tile then the B tile). This
-// wave's A loads read MOE_AADDR(k0) + aoff[j] (aptr[j] + 2 k0 when WIDE), its
-// B loads MOE_BADDR(k0) + boff[j]; MOE_LOADA / MOE_LOADB read one 16-k step
-// of MFMA operands from a stage into fa / fb; MOE_PRE_MFMA may edit them
-// before the step's MFMAs; the scheduler is asked to place MOE_READS_AFTER(q)
-// LDS reads of the next step after the step's q-th MFMA.
+// kernel's instruction schedule): KT >= 1 stages of MBK through an LDS ring
+// of NST stages (NST = 2 or 3; stage s at LDS address Ls[s], the A tile of
+// TBM rows then the B tile; SA / SB point at them), NST - 1 stages in flight
+// while one is computed. This wave's TLPW A loads read MOE_AADDR(k0) +
+// aoff[j] (aptr[j] + 2 k0 when WIDE), its LPWB B loads MOE_BADDR(k0) +
+// boff[j]; MOE_LOADA / MOE_LOADB read
+// one 16-k step of MFMA operands from a stage into fa / fb (MOE_LOADA for the
+// first MIA row blocks); MOE_PRE_MFMA may edit them before the step's MFMAs;
+// the scheduler is asked to place MOE_READS_AFTER(q, MIA) LDS reads of the
+// next step after the step's q-th MFMA. MIA <= MI row blocks of 32 take part
+// (a tile whose rows fit the first MIA blocks skips the others' MFMAs).
 // Every kernel defines these hooks before it expands MOE_PIPELINE.
 #define MOE_ISSUE(ST, K0)                                                               \
   do {                                                                                  \
-    const uint32_t la_ = ((ST) ? L1 : L0) + (uint32_t)(MLPW * wave) * 1024u;            \
-    const uint32_t lb_ = ((ST) ? L1 : L0) + MBM * CH * 16 + (uint32_t)(LPWB * wave) * 1024u; \
-    _Pragma("unroll") for (int j = 0; j < MLPW; ++j) {                                  \
+    const uint32_t la_ = Ls[ST] + (uint32_t)(TLPW * wave) * 1024u;                      \
+    const uint32_t lb_ = Ls[ST] + TBM * CH * 16 + (uint32_t)(LPWB * wave) * 1024u;      \
+    _Pragma("unroll") for (int j = 0; j < TLPW; ++j) {                                  \
       if (WIDE) lds_dma16(aptr[WIDE ? j : 0] + (K0) * 2, la_ + j * 1024);               \
       else lds_dma16(MOE_AADDR(K0), aoff[j], la_ + j * 1024);                           \
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < LPWB; ++j)                                    \
       lds_dma16(MOE_BADDR(K0), boff[j], lb_ + j * 1024);                                \
   } while (0)
-#define MOE_LOADF(SLOT, ST, KS) \
-  do {                          \
-    MOE_LOADA(SLOT, ST, KS);    \
-    MOE_LOADB(SLOT, ST, KS);    \
+#define MOE_LOADF(SLOT, ST, KS, MIA) \
+  do {                               \
+    MOE_LOADA(SLOT, ST, KS, MIA);    \
+    MOE_LOADB(SLOT, ST, KS);         \
   } while (0)
 // operands of k-contiguous tiles ([row][MBK k], 16-byte chunk XOR swizzles)
-#define MOE_LOADA_ROWS(SLOT, ST, KS)                                                   \
+#define MOE_LOADA_ROWS(SLOT, ST, KS, MIA)                                              \
   do {                                                                                 \
     const int chunk_ = (KS) * 2 + (lane >> 5);                                         \
-    _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) fa[SLOT][mi] = as_bf16x8(        \
+    _Pragma("unroll") for (int mi = 0; mi < (MIA); ++mi) fa[SLOT][mi] = as_bf16x8(     \
         SA[ST][arow[mi] * CH + (chunk_ ^ ((arow[mi] >> 1) & 7))]);                     \
   } while (0)
 #define MOE_LOADB_ROWS(SLOT, ST, KS)                                                   \
@@ -153,59 +175,60 @@ template <int WT> struct BTile {
     }                                                                                  \
   } while (0)
 // operands of k-major tiles ([MBK k][256 columns], see kmajor_frag)
-#define MOE_LOADA_KMAJOR(SLOT, ST, KS)                                                 \
+#define MOE_LOADA_KMAJOR(SLOT, ST, KS, MIA)                                            \
   do {                                                                                 \
-    _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) fa[SLOT][mi] =                   \
-        kmajor_frag(((ST) ? L1 : L0), acol[mi], (KS), lane);                           \
+    _Pragma("unroll") for (int mi = 0; mi < (MIA); ++mi) fa[SLOT][mi] =                \
+        kmajor_frag(Ls[ST], acol[mi], (KS), lane);                                     \
   } while (0)
 #define MOE_LOADB_KMAJOR(SLOT, ST, KS)                                                 \
   do {                                                                                 \
     _Pragma("unroll") for (int s = 0; s < NI; ++s) fb[SLOT][s] =                       \
-        kmajor_frag(((ST) ? L1 : L0) + MBM * CH * 16, bcol[s], (KS), lane);            \
+        kmajor_frag(Ls[ST] + TBM * CH * 16, bcol[s], (KS), lane);                      \
   } while (0)
-// a do-while keeps the compiler from carrying a zero-trip copy of the
-// accumulators across the loop
-#define MOE_PIPELINE(KT_)                                                                 \
+// Stage kt lives in buffer kt % NST. The first NST stages are issued up
+// front; after stage kt is computed, once stage kt+1 has landed for every
+// wave (later stages may still be in flight) and nobody reads stage kt any
+// more, its buffer is refilled with stage kt + NST. A do-while keeps the
+// compiler from carrying a zero-trip copy of the accumulators across the loop.
+#define MOE_PIPELINE(KT_, MIA)                                                            \
   do {                                                                                    \
     const int KT = (KT_);                                                                 \
-    MOE_ISSUE(0, 0);                                                                      \
-    if (KT > 1) MOE_ISSUE(1, MBK);                                                        \
-    if (KT > 1) wait_vmcnt<MLPW + LPWB>(); else wait_vmcnt<0>();                          \
+    _Pragma("unroll") for (int s_ = 0; s_ < NST; ++s_)                                    \
+      if (s_ < KT) MOE_ISSUE(s_, s_ * MBK);                                                \
+    wait_landed<TLPW + LPWB>(min(NST - 1, KT - 1));                                       \
     block_sync();                                                                         \
-    MOE_LOADF(0, 0, 0);                                                                   \
+    MOE_LOADF(0, 0, 0, MIA);                                                              \
     int kt0 = 0;                                                                          \
     do {                                                                                  \
-      _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                     \
+      _Pragma("unroll") for (int u = 0; u < NST; ++u) {                                   \
         const int kt = kt0 + u;                                                           \
         if (kt < KT) {                                                                    \
           _Pragma("unroll") for (int ks = 0; ks < NKS; ++ks) {                            \
             const int slot = ks & 1;                                                      \
             if (ks + 1 < NKS) {                                                           \
-              MOE_LOADF(slot ^ 1, u, ks + 1);                                             \
+              MOE_LOADF(slot ^ 1, u, ks + 1, MIA);                                        \
             } else if (kt + 1 < KT) {                                                     \
-              /* stage kt+1 landed for every wave and nobody reads stage kt any */        \
-              /* more: refill stage kt's buffer with stage kt+2 */                        \
-              wait_vmcnt<0>();                                                            \
+              wait_landed<TLPW + LPWB>(min(NST - 2, KT - 2 - kt));                        \
               wait_lgkmcnt0();                                                            \
               block_sync();                                                               \
-              if (kt + 2 < KT) MOE_ISSUE(u, (kt + 2) * MBK);                              \
-              MOE_LOADF(slot ^ 1, u ^ 1, 0);                                              \
+              if (kt + NST < KT) MOE_ISSUE(u, (kt + NST) * MBK);                          \
+              MOE_LOADF(slot ^ 1, (u + 1) % NST, 0, MIA);                                 \
             }                                                                             \
             MOE_PRE_MFMA(slot, kt, ks);                                                   \
-            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                             \
+            _Pragma("unroll") for (int mi = 0; mi < (MIA); ++mi)                          \
               _Pragma("unroll") for (int s = 0; s < NI; ++s)                              \
                 acc[mi][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                     \
                     fa[slot][mi], fb[slot][s], acc[mi][s], 0, 0, 0);                      \
-            /* one MFMA, then MOE_READS_AFTER(q) LDS reads of the next step */            \
-            _Pragma("unroll") for (int q = 0; q < MI * NI; ++q) {                         \
+            /* one MFMA, then MOE_READS_AFTER(q, MIA) LDS reads of the next step */       \
+            _Pragma("unroll") for (int q = 0; q < (MIA) * NI; ++q) {                      \
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          \
-              _Pragma("unroll") for (int r_ = 0; r_ < MOE_READS_AFTER(q); ++r_)           \
+              _Pragma("unroll") for (int r_ = 0; r_ < MOE_READS_AFTER(q, MIA); ++r_)      \
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        \
             }                                                                             \
           }                                                                               \
         }                                                                                 \
       }                                                                                   \
-      kt0 += 2;                                                                           \
+      kt0 += NST;                                                                         \
     } while (kt0 < KT);                                                                   \
   } while (0)
 
@@ -313,21 +336,35 @@ MOE_DEV void stage_mid() {
 
 // WIDE: the gathered activation rows are addressed with 64-bit per-lane
 // pointers (x larger than 2 GiB); otherwise with 32-bit offsets from x.
-template <int MODE, int WT, bool WIDE>
-__global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t n_ntiles) {
+// Tile shapes (TBM activation rows x BN weight rows): the wide tiles, 256 x
+// 256, for experts with more than kStreamRows rows; the stream tiles, 128 x
+// 512, for experts with at most kStreamRows rows (one row tile each), whose
+// weights are read once per launch from HBM while their few activation rows
+// are re-read from L2 for each column tile: the wider the tile, the fewer
+// those re-reads (two stages of 16 + 64 KB fill the 160 KB of LDS).
+// CLS: which experts the launch covers (kClsAll, kClsStream, kClsWide).
+template <int MODE, int WT, bool WIDE, int TBM, int BN>
+__global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t n_ntiles,
+                                                            int cls) {
   constexpr bool GATEUP = MODE == M_GATEUP || MODE == M_GATEUP_SAVE;
   constexpr bool I8 = WT == WT_I8;
-  constexpr int ESZ = BTile<WT>::ESZ, BCH = BTile<WT>::BCH, LPWB = BTile<WT>::LPW;
+  constexpr int NST = 2;
+  constexpr int TLPW = TBM * 8 / 64 / MNW;     // A LDS-DMA loads per wave per stage
+  constexpr int ESZ = BTile<WT, BN>::ESZ, BCH = BTile<WT, BN>::BCH, LPWB = BTile<WT, BN>::LPW;
   constexpr int CH = MBK / 8;                   // 16-byte chunks per A row (bf16)
-  constexpr int MWM = WaveGrid<WT>::M, MWN = WaveGrid<WT>::N;
-  constexpr int MW = MBM / MWM, NWR = MNB / MWN;
-  constexpr int MI = MW / 32, NI = NWR / 32;    // 8 accumulators: 2 x 4 (bf16) or 4 x 2 (int8)
+  constexpr int MWM = WaveGrid<WT, TBM, BN>::M, MWN = WaveGrid<WT, TBM, BN>::N;
+  constexpr int NWR = BN / MWN;                 // weight rows per wave
+  constexpr int MI = TBM / MWM / 32, NI = NWR / 32;
   constexpr int NKS = MBK / 16;
+  static_assert(MI >= 2 && MI % 2 == 0, "a half tile takes half of each wave's row blocks");
+  static_assert(!GATEUP || NI % 2 == 0, "a wave takes gate and up blocks in pairs");
+  static_assert(TBM * BN <= MBM * MNB, "a split piece's partial tile fits one scratch slot");
   // one LDS variable per stage: the A tile then the B tile
-  __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
+  constexpr int STG = TBM * CH + BN * BCH;
+  __shared__ u32x4 sT0[STG], sT1[STG];
   u32x4* const SA[2] = {sT0, sT1};
-  u32x4* const SB[2] = {sT0 + MBM * CH, sT1 + MBM * CH};
-  const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
+  u32x4* const SB[2] = {sT0 + TBM * CH, sT1 + TBM * CH};
+  const uint32_t Ls[2] = {lds_addr(sT0), lds_addr(sT1)};
 
   const int N = GATEUP ? a.F : a.H;
   const int K = GATEUP ? a.H : a.F;
@@ -335,17 +372,18 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   int piece = -1, npieces = 1;
   GroupedTile tile;
   if (GATEUP) {
-    // (with 128 output columns per tile the Grok-1 shape's 256 column tiles
-    // fill whole rounds of every XCD)
-    if (!xcd_tile_index(a.offsets, a.E, MBM, n_ntiles, lin)) return;
+    // (with 128 output columns per wide tile the Grok-1 shape's 256 column
+    // tiles fill whole rounds of every XCD)
+    if (!xcd_tile_index(a.offsets, a.E, TBM, n_ntiles, cls, lin)) return;
   } else {
-    if (!xcd_tail_work(a.offsets, a.E, MBM, n_ntiles, K / MBK, lin, piece, npieces, pslot)) return;
+    if (!xcd_tail_work(a.offsets, a.E, TBM, n_ntiles, cls, K / MBK, lin, piece, npieces, pslot))
+      return;
   }
-  if (!grouped_tile(a.offsets, a.E, MBM, n_ntiles, lin, tile)) return;
+  if (!grouped_tile(a.offsets, a.E, TBM, n_ntiles, cls, lin, tile)) return;
   // k stages of this work item (a piece of a split tail tile, or all)
   const int kb = piece >= 0 ? piece * (K / MBK) / npieces : 0;
   const int ke = piece >= 0 ? (piece + 1) * (K / MBK) / npieces : K / MBK;
-  constexpr int BNO = GATEUP ? MNB / 2 : MNB;  // output columns per tile
+  constexpr int BNO = GATEUP ? BN / 2 : BN;  // output columns per tile
   const int e = __builtin_amdgcn_readfirstlane(tile.e);
   const int m0 = __builtin_amdgcn_readfirstlane(tile.m0);
   const int m_end = __builtin_amdgcn_readfirstlane(tile.m_end);
@@ -362,11 +400,11 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
   const char* const abase = GATEUP ? uniform_ptr(a.x)
                                    : uniform_ptr(static_cast<const char*>(a.h) +
                                                  (int64_t)m0 * a.F * 2 + (int64_t)kb * MBK * 2);
-  uint32_t aoff[MLPW];
-  const char* aptr[WIDE ? MLPW : 1];
+  uint32_t aoff[TLPW];
+  const char* aptr[WIDE ? TLPW : 1];
 #pragma unroll
-  for (int j = 0; j < MLPW; ++j) {
-    const int q = (MLPW * wave + j) * 64 + lane;
+  for (int j = 0; j < TLPW; ++j) {
+    const int q = (TLPW * wave + j) * 64 + lane;
     const int r = q / CH, c = (q % CH) ^ ((r >> 1) & 7);
     const int row = min(m0 + r, m_end - 1);
     if (GATEUP) {
@@ -377,9 +415,9 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
       aoff[j] = (uint32_t)(row - m0) * (uint32_t)(a.F * 2) + c * 16;
     }
   }
-  // B: one weight matrix per wave. Each wave loads 32 consecutive B-tile
-  // rows; with GATEUP, waves [0, MNW/2) load the gate rows (tile rows
-  // [0, MNB/2)) and the others the up rows of the same output columns.
+  // B: one weight matrix per wave. Each wave loads consecutive B-tile rows;
+  // with GATEUP, waves [0, MNW/2) load the gate rows (tile rows [0, BN/2))
+  // and the others the up rows of the same output columns.
   const void* const wmat = GATEUP ? (wave < MNW / 2 ? a.wg : a.wu) : a.wd;
   const char* const bbase = uniform_ptr(static_cast<const char*>(wmat) +
                                         (((int64_t)e * N + n0) * K + (int64_t)kb * MBK) * ESZ);
@@ -389,19 +427,27 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
     const int q = (LPWB * wave + j) * 64 + lane;
     const int r = q / BCH;
     const int c = I8 ? (q % BCH) ^ ((r >> 2) & 3) : (q % BCH) ^ ((r >> 1) & 7);
-    const int rr = GATEUP ? (r & (MNB / 2 - 1)) : r;
+    const int rr = GATEUP ? (r & (BN / 2 - 1)) : r;
     const int n = min(n0 + rr, N - 1) - n0;
     boff[j] = (uint32_t)n * (uint32_t)(K * ESZ) + c * 16;
   }
 
+  // Rows: wave (wm, wn) owns the row blocks mi * RB + wm * 32 .. + 31 (RB =
+  // 32 * MWM, mi < MI). The blocks of all waves interleave, so that in a
+  // partial tile (an expert's last) the blocks that hold no row are spread
+  // over the waves: a wave whose rows fit its first MI / 2 blocks skips the
+  // MFMAs of the others. Waves w and w + 4 share a SIMD, so a wide bf16 tile
+  // of at most 128 rows halves every SIMD's MFMA work, one of at most 192
+  // rows cuts the busiest SIMD's by a quarter.
+  constexpr int RB = 32 * MWM;
   const int wm = wave / MWN, wn = wave % MWN;
   int arow[MI], brow[NI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) arow[mi] = wm * MW + mi * 32 + (lane & 31);
+  for (int mi = 0; mi < MI; ++mi) arow[mi] = mi * RB + wm * 32 + (lane & 31);
 #pragma unroll
   for (int s = 0; s < NI; ++s)
     brow[s] = (GATEUP ? (s < NI / 2 ? wn * (NWR / 2) + s * 32
-                                    : MNB / 2 + wn * (NWR / 2) + (s - NI / 2) * 32)
+                                    : BN / 2 + wn * (NWR / 2) + (s - NI / 2) * 32)
                       : wn * NWR + s * 32) + (lane & 31);
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -418,8 +464,14 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
 #define MOE_LOADA MOE_LOADA_ROWS
 #define MOE_LOADB MOE_LOADB_ROWS
 #define MOE_PRE_MFMA(SLOT, KT_, KS)
-#define MOE_READS_AFTER(q) ((q) < MI + NI ? 1 : 0)
-  MOE_PIPELINE(ke - kb);
+#define MOE_READS_AFTER(q, MIA) ((q) < (MIA) + NI ? 1 : 0)
+  // row blocks of this wave that start before the tile's end (they come first)
+  int mia = 0;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+    if (m0 + mi * RB + wm * 32 < m_end) mia = mi + 1;
+  if (mia <= MI / 2) MOE_PIPELINE(ke - kb, MI / 2);
+  else MOE_PIPELINE(ke - kb, MI);
 #undef MOE_AADDR
 #undef MOE_BADDR
 #undef MOE_LOADA
@@ -428,13 +480,14 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
 #undef MOE_READS_AFTER
 
   // epilogue; 32x32 accumulator layout: lane l holds column l%32, register
-  // v holds row 8*(v/4) + 4*(l/32) + v%4
+  // v holds row 8*(v/4) + 4*(l/32) + v%4 of the block (rows past m_end,
+  // including the blocks a half tile skipped, are not written)
   const int jcol = lane & 31;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int r = m0 + wm * MW + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int r = m0 + mi * RB + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (r >= m_end) continue;
       if (GATEUP) {
         uint16_t* hrow = static_cast<uint16_t*>(a.h) + (int64_t)r * a.F;
@@ -455,9 +508,9 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
           }
         }
       } else if (piece >= 0) {
-        // a piece of a split tail tile: float32 partial tile, summed (and
-        // scaled) by tail_reduce_kernel
-        float* prow = static_cast<float*>(a.ws) + (int64_t)pslot * MBM * MNB + (r - m0) * MNB;
+        // a piece of a split tail tile: float32 partial tile [TBM][BN],
+        // summed (and scaled) by tail_reduce_kernel
+        float* prow = static_cast<float*>(a.ws) + (int64_t)pslot * MBM * MNB + (r - m0) * BN;
 #pragma unroll
         for (int s = 0; s < NI; ++s) prow[wn * NWR + s * 32 + jcol] = acc[mi][s][v];
       } else {
@@ -477,7 +530,8 @@ __global__ __launch_bounds__(MNW * 64) void ffn_mfma_kernel(FfnArgs a, uint32_t 
 // The split tail tiles of a tail-split launch (the down projection, the data
 // gradients): y[r][n] = the pieces' float32 partials summed in piece order
 // (times scale[e][n] when scale is set), rounded once to bf16. A tail tile
-// is reduced by kReduceParts work-groups, one float4 of it per thread.
+// (TBM x BN, in a scratch slot of MBM x MNB floats) is reduced by
+// kReduceParts work-groups, one float4 of it per thread.
 struct TailReduce {
   const int32_t* offsets;
   int E;
@@ -486,61 +540,93 @@ struct TailReduce {
   const float* ws;
   void* y;        // [rows][N] bf16
   const float* scale;   // [E][N] or null
+  int cls;        // the launch's expert class
 };
 constexpr int kReduceParts = MBM * MNB / 4 / 256;
 
+template <int TBM, int BN>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduce t, uint32_t n_ntiles) {
   const uint32_t part = blockIdx.x % kReduceParts, tj = blockIdx.x / kReduceParts;
   const uint32_t xcd = tj / kCusPerXcd, j = tj % kCusPerXcd;
-  const TailPlan p = tail_plan(t.offsets, t.E, MBM, n_ntiles, xcd, t.kstages);
+  const TailPlan p = tail_plan(t.offsets, t.E, TBM, n_ntiles, t.cls, xcd, t.kstages);
   if (p.S <= 1 || j >= p.tail) return;
   GroupedTile tile;
-  if (!grouped_tile(t.offsets, t.E, MBM, n_ntiles, p.base + p.full + j, tile)) return;
-  const int q = (int)part * 256 + (int)threadIdx.x;   // float4 of the tile
-  const int r = tile.m0 + q / (MNB / 4), n = tile.nt * MNB + (q % (MNB / 4)) * 4;
-  if (r >= tile.m_end || n >= t.N) return;
-  const float4* src = reinterpret_cast<const float4*>(t.ws) +
-                      (int64_t)(xcd * kTailSlots + j * p.S) * (MBM * MNB / 4) + q;
-  float4 v = src[0];
+  if (!grouped_tile(t.offsets, t.E, TBM, n_ntiles, t.cls, p.base + p.full + j, tile)) return;
+  const float4* src0 = reinterpret_cast<const float4*>(t.ws) +
+                       (int64_t)(xcd * kTailSlots + j * p.S) * (MBM * MNB / 4);
+  static_assert(TBM * BN == MBM * MNB, "one float4 of the tile per thread");
+  {
+    const int q = (int)part * 256 + (int)threadIdx.x;   // float4 of the tile
+    const int r = tile.m0 + q / (BN / 4), n = tile.nt * BN + (q % (BN / 4)) * 4;
+    if (r >= tile.m_end || n >= t.N) return;
+    const float4* src = src0 + q;
+    float4 v = src[0];
 #pragma unroll
-  for (uint32_t pc = 1; pc < kTailMaxPieces; ++pc) {
-    if (pc < p.S) {
-      const float4 w = src[(int64_t)pc * (MBM * MNB / 4)];
-      v.x += w.x;
-      v.y += w.y;
-      v.z += w.z;
-      v.w += w.w;
+    for (uint32_t pc = 1; pc < kTailMaxPieces; ++pc) {
+      if (pc < p.S) {
+        const float4 w = src[(int64_t)pc * (MBM * MNB / 4)];
+        v.x += w.x;
+        v.y += w.y;
+        v.z += w.z;
+        v.w += w.w;
+      }
     }
-  }
-  const float o[4] = {v.x, v.y, v.z, v.w};
-  uint16_t* yrow = static_cast<uint16_t*>(t.y) + (int64_t)r * t.N;
+    const float o[4] = {v.x, v.y, v.z, v.w};
+    uint16_t* yrow = static_cast<uint16_t*>(t.y) + (int64_t)r * t.N;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (n + c >= t.N) break;
-    const float sc = t.scale ? t.scale[(int64_t)tile.e * t.N + n + c] : 1.f;
-    yrow[n + c] = f32_to_bf16_bits(t.scale ? o[c] * sc : o[c]);
+    for (int c = 0; c < 4; ++c) {
+      if (n + c >= t.N) break;
+      const float sc = t.scale ? t.scale[(int64_t)tile.e * t.N + n + c] : 1.f;
+      yrow[n + c] = f32_to_bf16_bits(t.scale ? o[c] * sc : o[c]);
+    }
   }
 }
 
+template <int TBM, int BN>
 hipError_t launch_tail_reduce(const TailReduce& t, uint32_t n_ntiles, hipStream_t s) {
-  hipLaunchKernelGGL(tail_reduce_kernel, dim3(8 * kCusPerXcd * kReduceParts), dim3(256), 0, s, t,
-                     n_ntiles);
+  hipLaunchKernelGGL((tail_reduce_kernel<TBM, BN>), dim3(8 * kCusPerXcd * kReduceParts),
+                     dim3(256), 0, s, t, n_ntiles);
   return hipGetLastError();
 }
 
-template <int MODE, int WT, bool WIDE>
-hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
+// One launch of the forward GEMM over one class of experts (and, for the
+// down projection, the reduce of its split tail tiles).
+template <int MODE, int WT, bool WIDE, int TBM, int BN>
+hipError_t launch_mfma(const FfnArgs& a, int cls, hipStream_t s) {
   constexpr bool GATEUP = MODE == M_GATEUP || MODE == M_GATEUP_SAVE;
-  const uint32_t nt = GATEUP ? (uint32_t)((a.F + MNB / 2 - 1) / (MNB / 2))
-                             : (uint32_t)((a.H + MNB - 1) / MNB);
-  const unsigned grid = grouped_grid(a.T * a.k, a.E, MBM, nt) + (GATEUP ? 0 : kTailExtraBlocks);
-  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WT, WIDE>), dim3(grid), dim3(MNW * 64), 0, s, a, nt);
+  const uint32_t nt = GATEUP ? (uint32_t)((a.F + BN / 2 - 1) / (BN / 2))
+                             : (uint32_t)((a.H + BN - 1) / BN);
+  // worst case: every assignment (stream class: one row tile per expert)
+  const unsigned tiles = cls == kClsStream ? (unsigned)((a.E * nt + 7) / 8 * 8)
+                                           : grouped_grid(a.T * a.k, a.E, TBM, nt);
+  const unsigned grid = tiles + (GATEUP ? 0 : kTailExtraBlocks);
+  hipLaunchKernelGGL((ffn_mfma_kernel<MODE, WT, WIDE, TBM, BN>), dim3(grid), dim3(MNW * 64), 0,
+                     s, a, nt, cls);
   if (GATEUP) return hipGetLastError();
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const TailReduce t{a.offsets, a.E, a.H, a.F / MBK, static_cast<const float*>(a.ws), a.y,
-                     WT == WT_I8 ? a.sd : nullptr};
-  return launch_tail_reduce(t, nt, s);
+                     WT == WT_I8 ? a.sd : nullptr, cls};
+  return launch_tail_reduce<TBM, BN>(t, nt, s);
+}
+
+// The forward GEMM over all experts: those with more than kStreamRows rows on
+// the wide tiles, those with at most kStreamRows rows on the stream tiles. The
+// split is made on the device from the dispatch offsets (each launch's
+// work-groups find their class's tiles there). Above a mean of
+// kStreamMeanRows rows per expert (known on the host: T k / E) every expert
+// takes the wide tiles: an expert with at most kStreamRows rows is then an
+// outlier, and the two stream launches, empty in the common case, cost 30 to
+// 85 us per layer (measured at 2048 and 8192 tokens).
+constexpr int64_t kStreamMeanRows = 256;
+
+template <int MODE, int WT, bool WIDE>
+hipError_t launch_mfma_all(const FfnArgs& a, hipStream_t s) {
+  if (a.T * a.k > (int64_t)a.E * kStreamMeanRows)
+    return launch_mfma<MODE, WT, WIDE, MBM, MNB>(a, kClsAll, s);
+  hipError_t e = launch_mfma<MODE, WT, WIDE, MBM, MNB>(a, kClsWide, s);
+  if (e != hipSuccess) return e;
+  return launch_mfma<MODE, WT, WIDE, kStreamRows, 2 * MNB>(a, kClsStream, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,13 +646,16 @@ hipError_t launch_mfma(const FfnArgs& a, hipStream_t s) {
 // [E][m_split][N], the rest to out1 [E][M - m_split][N], bf16.
 __global__ __launch_bounds__(MNW * 64) void wgrad_tn_kernel(WgradTnArgs w) {
   constexpr bool WIDE = false;
+  constexpr int NST = 2;
   constexpr int CH = MBK / 8, NKS = MBK / 16;
-  constexpr int BCH = BTile<WT_BF16>::BCH, LPWB = BTile<WT_BF16>::LPW;
-  constexpr int MWM = WaveGrid<WT_BF16>::M, MWN = WaveGrid<WT_BF16>::N;
+  constexpr int BCH = BTile<WT_BF16, MNB>::BCH, LPWB = BTile<WT_BF16, MNB>::LPW;
+  constexpr int MWM = WaveGrid<WT_BF16, MBM, MNB>::M, MWN = WaveGrid<WT_BF16, MBM, MNB>::N;
+  constexpr int TBM = MBM, TLPW = MLPW;
   constexpr int MW = MBM / MWM, NWR = MNB / MWN;
   constexpr int MI = MW / 32, NI = NWR / 32;
   __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
   const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
+  const uint32_t Ls[2] = {L0, L1};
   const char* const* aptr = nullptr;
 
   const uint32_t MT = (uint32_t)(w.M + MBM - 1) / MBM, NT = (uint32_t)(w.N + MNB - 1) / MNB;
@@ -630,9 +719,9 @@ __global__ __launch_bounds__(MNW * 64) void wgrad_tn_kernel(WgradTnArgs w) {
     }                                                                            \
   } while (0)
 // 12 reads per step after 8 MFMAs (other placements measured the same)
-#define MOE_READS_AFTER(q) ((q) < 4 ? 2 : 1)
+#define MOE_READS_AFTER(q, MIA) ((q) < 4 ? 2 : 1)
   // an expert without rows has a zero gradient: no stage, zeros written
-  if (kt > 0) MOE_PIPELINE(kt);
+  if (kt > 0) MOE_PIPELINE(kt, MI);
 #undef MOE_AADDR
 #undef MOE_BADDR
 #undef MOE_LOADA
@@ -676,22 +765,25 @@ __global__ __launch_bounds__(MNW * 64) void wgrad_tn_kernel(WgradTnArgs w) {
 // a k-major tile read through transposing LDS reads.
 __global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_t n_ntiles) {
   constexpr bool WIDE = false;
+  constexpr int NST = 2;
   constexpr int CH = MBK / 8, NKS = MBK / 16;
-  constexpr int BCH = BTile<WT_BF16>::BCH, LPWB = BTile<WT_BF16>::LPW;
-  constexpr int MWM = WaveGrid<WT_BF16>::M, MWN = WaveGrid<WT_BF16>::N;
+  constexpr int BCH = BTile<WT_BF16, MNB>::BCH, LPWB = BTile<WT_BF16, MNB>::LPW;
+  constexpr int MWM = WaveGrid<WT_BF16, MBM, MNB>::M, MWN = WaveGrid<WT_BF16, MBM, MNB>::N;
+  constexpr int TBM = MBM, TLPW = MLPW;
   constexpr int MW = MBM / MWM, NWR = MNB / MWN;
   constexpr int MI = MW / 32, NI = NWR / 32;
   __shared__ u32x4 sT0[MBM * CH + MNB * BCH], sT1[MBM * CH + MNB * BCH];
   u32x4* const SA[2] = {sT0, sT1};
-  const uint32_t L0 = lds_addr(sT0), L1 = lds_addr(sT1);
+  const uint32_t Ls[2] = {lds_addr(sT0), lds_addr(sT1)};
   const char* const* aptr = nullptr;
 
   uint32_t lin, pslot = 0;
   int piece = -1, npieces = 1;
   GroupedTile tile;
-  if (!xcd_tail_work(d.offsets, d.E, MBM, n_ntiles, d.K / MBK, lin, piece, npieces, pslot))
+  if (!xcd_tail_work(d.offsets, d.E, MBM, n_ntiles, kClsAll, d.K / MBK, lin, piece, npieces,
+                     pslot))
     return;
-  if (!grouped_tile(d.offsets, d.E, MBM, n_ntiles, lin, tile)) return;
+  if (!grouped_tile(d.offsets, d.E, MBM, n_ntiles, kClsAll, lin, tile)) return;
   // k range of this work item (a piece of a split tail tile, or all)
   const int kb = piece >= 0 ? piece * (d.K / MBK) / npieces : 0;
   const int ke = piece >= 0 ? (piece + 1) * (d.K / MBK) / npieces : d.K / MBK;
@@ -745,8 +837,8 @@ __global__ __launch_bounds__(MNW * 64) void dgrad_nn_kernel(DgradArgs d, uint32_
 #define MOE_LOADA MOE_LOADA_ROWS
 #define MOE_LOADB MOE_LOADB_KMAJOR
 #define MOE_PRE_MFMA(SLOT, KT_, KS)
-#define MOE_READS_AFTER(q) ((q) + MI * NI < MI + 2 * NI ? 2 : (q) < MI + 2 * NI ? 1 : 0)
-  MOE_PIPELINE(ke - kb);
+#define MOE_READS_AFTER(q, MIA) ((q) + MI * NI < MI + 2 * NI ? 2 : (q) < MI + 2 * NI ? 1 : 0)
+  MOE_PIPELINE(ke - kb, MI);
 #undef MOE_AADDR
 #undef MOE_BADDR
 #undef MOE_LOADA
@@ -803,21 +895,21 @@ size_t tiled_ws_bytes() { return kTailScratchBytes; }
 hipError_t launch_gateup_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
   if (wt == WT_I4) return hipErrorNotSupported;   // int4: decode kernels only
   if (x_needs_wide(a))
-    return wt == WT_I8 ? launch_mfma<M_GATEUP, WT_I8, true>(a, s)
-                       : launch_mfma<M_GATEUP, WT_BF16, true>(a, s);
-  return wt == WT_I8 ? launch_mfma<M_GATEUP, WT_I8, false>(a, s)
-                     : launch_mfma<M_GATEUP, WT_BF16, false>(a, s);
+    return wt == WT_I8 ? launch_mfma_all<M_GATEUP, WT_I8, true>(a, s)
+                       : launch_mfma_all<M_GATEUP, WT_BF16, true>(a, s);
+  return wt == WT_I8 ? launch_mfma_all<M_GATEUP, WT_I8, false>(a, s)
+                     : launch_mfma_all<M_GATEUP, WT_BF16, false>(a, s);
 }
 
 hipError_t launch_down_tiled(const FfnArgs& a, Wt wt, hipStream_t s) {
   if (wt == WT_I4) return hipErrorNotSupported;
-  return wt == WT_I8 ? launch_mfma<M_DOWN, WT_I8, false>(a, s)
-                     : launch_mfma<M_DOWN, WT_BF16, false>(a, s);
+  return wt == WT_I8 ? launch_mfma_all<M_DOWN, WT_I8, false>(a, s)
+                     : launch_mfma_all<M_DOWN, WT_BF16, false>(a, s);
 }
 
 hipError_t launch_gateup_save_tiled(const FfnArgs& a, hipStream_t s) {
-  return x_needs_wide(a) ? launch_mfma<M_GATEUP_SAVE, WT_BF16, true>(a, s)
-                         : launch_mfma<M_GATEUP_SAVE, WT_BF16, false>(a, s);
+  return x_needs_wide(a) ? launch_mfma_all<M_GATEUP_SAVE, WT_BF16, true>(a, s)
+                         : launch_mfma_all<M_GATEUP_SAVE, WT_BF16, false>(a, s);
 }
 
 hipError_t launch_wgrad_tn(const WgradTnArgs& w, hipStream_t s) {
@@ -836,8 +928,8 @@ hipError_t launch_dgrad_nn(const DgradArgs& d, hipStream_t s) {
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const TailReduce t{d.offsets, d.E, d.N, d.K / MBK, static_cast<const float*>(d.ws), d.y,
-                     nullptr};
-  return launch_tail_reduce(t, nt, s);
+                     nullptr, kClsAll};
+  return launch_tail_reduce<MBM, MNB>(t, nt, s);
 }
 
 

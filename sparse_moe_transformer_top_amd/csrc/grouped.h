@@ -4,7 +4,8 @@
 // launch covers, per expert, ceil(n_e / BM) row tiles times n_ntiles column
 // tiles; the grid is sized on the host for the worst case (ceil(N/BM) + E row
 // tiles in total, N = T*k), so no host synchronisation is needed to learn the
-// counts, and work-groups past the real tile count exit at once. Within an
+// counts, and work-groups past the real tile count exit at once. A launch
+// may cover one class of experts (by row count, see in_class). Within an
 // expert the row tile varies fastest, so the work-groups sharing one weight
 // tile run next to each other (on one XCD, see xcd_tile_index) and read it
 // through the same L2.
@@ -12,6 +13,24 @@
 #include "common.h"
 
 namespace moe {
+
+// Expert classes of a launch: every expert; the experts with at most
+// kStreamRows rows (one row tile each of the stream tiles); the experts with
+// more.
+constexpr int kClsAll = 0;
+constexpr int kClsStream = 1;
+constexpr int kClsWide = 2;
+constexpr int kStreamRows = 128;
+
+MOE_DEV bool in_class(int n, int cls) {
+  return cls == kClsAll || (cls == kClsStream ? n <= kStreamRows : n > kStreamRows);
+}
+
+// Row tiles of BM rows over expert e's rows [lo, hi) in the launch's class.
+MOE_DEV uint32_t class_row_tiles(int lo, int hi, int BM, int cls) {
+  const int n = hi - lo;
+  return in_class(n, cls) ? (uint32_t)((n + BM - 1) / BM) : 0u;
+}
 
 struct GroupedTile {
   int e;        // expert
@@ -21,11 +40,11 @@ struct GroupedTile {
 };
 
 MOE_DEV bool grouped_tile(const int32_t* __restrict__ offsets, int E, int BM, uint32_t n_ntiles,
-                          uint32_t lin, GroupedTile& out) {
+                          int cls, uint32_t lin, GroupedTile& out) {
   int lo = offsets[0];
   for (int e = 0; e < E; ++e) {
     const int hi = offsets[e + 1];
-    const uint32_t mt = (uint32_t)((hi - lo + BM - 1) / BM);
+    const uint32_t mt = class_row_tiles(lo, hi, BM, cls);
     const uint32_t cnt = mt * n_ntiles;
     if (lin < cnt) {
       out.e = e;
@@ -48,10 +67,9 @@ MOE_DEV bool grouped_tile(const int32_t* __restrict__ offsets, int E, int BM, ui
 // Work-groups past the end return false; grouped_tile() rejects an index past
 // R on the last XCD.
 MOE_DEV bool xcd_tile_index(const int32_t* __restrict__ offsets, int E, int BM,
-                            uint32_t n_ntiles, uint32_t& lin) {
+                            uint32_t n_ntiles, int cls, uint32_t& lin) {
   uint32_t R = 0;
-  for (int e = 0; e < E; ++e)
-    R += (uint32_t)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * n_ntiles;
+  for (int e = 0; e < E; ++e) R += class_row_tiles(offsets[e], offsets[e + 1], BM, cls) * n_ntiles;
   const uint32_t per = (R + 7) / 8, slot = blockIdx.x >> 3;
   if (slot >= per) return false;
   lin = (blockIdx.x & 7) * per + slot;
@@ -96,10 +114,9 @@ struct TailPlan {
 };
 
 MOE_DEV TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int BM, uint32_t n_ntiles,
-                           uint32_t xcd, int max_pieces) {
+                           int cls, uint32_t xcd, int max_pieces) {
   uint32_t R = 0;
-  for (int e = 0; e < E; ++e)
-    R += (uint32_t)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * n_ntiles;
+  for (int e = 0; e < E; ++e) R += class_row_tiles(offsets[e], offsets[e + 1], BM, cls) * n_ntiles;
   const uint32_t per = (R + 7) / 8;
   TailPlan t;
   t.base = xcd * per;
@@ -113,10 +130,10 @@ MOE_DEV TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int BM, u
 // This work-group's item: tile index lin, and piece (-1 for a whole tile) of
 // npieces, with its scratch slot. False for work-groups past the work.
 MOE_DEV bool xcd_tail_work(const int32_t* __restrict__ offsets, int E, int BM,
-                           uint32_t n_ntiles, int max_pieces, uint32_t& lin, int& piece,
+                           uint32_t n_ntiles, int cls, int max_pieces, uint32_t& lin, int& piece,
                            int& npieces, uint32_t& slot_out) {
   const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const TailPlan t = tail_plan(offsets, E, BM, n_ntiles, xcd, max_pieces);
+  const TailPlan t = tail_plan(offsets, E, BM, n_ntiles, cls, xcd, max_pieces);
   if (slot < t.full) {
     lin = t.base + slot;
     piece = -1;
@@ -135,7 +152,8 @@ MOE_DEV bool xcd_tail_work(const int32_t* __restrict__ offsets, int E, int BM,
 // Extra work-groups a tail-split launch may need beyond the tile grid: per
 // XCD, full + tail S <= (its tiles) + kTailSlots.
 constexpr unsigned kTailExtraBlocks = 8 * kTailSlots;
-// Float32 partial tiles of the split pieces (one 256 x 256 tile per slot).
+// Float32 partial tiles of the split pieces (one tile of up to 256 x 256
+// elements per slot).
 constexpr size_t kTailScratchBytes = (size_t)8 * kTailSlots * 256 * 256 * 4;
 
 // Worst-case grid, a multiple of 8 (see xcd_tile_index).

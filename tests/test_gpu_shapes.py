@@ -1,7 +1,7 @@
 """GPU parity for shapes beyond the Grok-1 defaults and for the ABI's stage
 entry points: other expert counts and k, the decode/tiled kernel boundary
-(T = 16 / 17), empty experts, and moe_expert_gate_up / moe_expert_down
-called on their own."""
+(T = 16 / 17), empty experts, experts with few rows on either tile shape, and
+moe_expert_gate_up / moe_expert_down called on their own."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from gpu_helpers import (check_close, check_dispatch_equal, check_routing, dev_tensor,
-                         host_array, log, out_as_f64, to_device)
+                         gpu_routing, host_array, log, out_as_f64, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -187,3 +187,42 @@ def test_layer_forward_equals_stage_calls(moe, name):
     ref = moe.moe_combine(y, disp["slot_row"], w)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("cf", [None, 1.0])
+def test_few_row_experts_above_the_stream_threshold(moe, cf):
+    # 2100 tokens over 8 experts: a mean of 525 rows per expert, above the
+    # 256 up to which experts with at most 128 rows take the stream tiles, so
+    # every expert runs on the wide tiles. The router makes three experts
+    # small (32, 60 and 40 rows: tiles that fit their first half) next to
+    # experts of 293 to 1212 rows; with cf = 1.0 the large ones drop rows.
+    cfg = synth.get_config("p_bf16").with_(name="few_rows", T=2100, H=256, F=512, seed=93,
+                                           capacity_factor=cf)
+    inp = synth.generate_host(cfg)
+    x = np.abs(oracle.widen(inp.x, "bf16")).astype(np.float32)
+    x[:, :2] = 0.0
+    x[:60, 0] = 1.0          # tokens 0..59 choose expert 6 first
+    x[60:100, 1] = 1.0       # tokens 60..99 choose expert 7 first
+    inp.x = synth.bf16_bits_from_f32(x)
+    for e, f in ((6, 0), (7, 1)):
+        inp.wr[e] = -np.abs(inp.wr[e])
+        inp.wr[e][f] = 50.0
+    d = to_device(inp)
+    out, ax = moe.moe_layer_forward(d["x"], d["wr"], d["wg"], d["wu"], d["wd"], k=2,
+                                    capacity_factor=cf, aux=True)
+    torch.cuda.synchronize()
+    res = oracle.layer_forward(inp.x, "bf16", inp.wr, inp.wg, inp.wu, inp.wd, "bf16", k=2,
+                               capacity_factor=cf)
+    own = gpu_routing(host_array(ax["topk_idx"]), host_array(ax["topk_w"]), res.routing)
+    if own is not None:
+        res = oracle.layer_forward(inp.x, "bf16", inp.wr, inp.wg, inp.wu, inp.wd, "bf16", k=2,
+                                   capacity_factor=cf, idx=own)
+    rows = np.diff(res.disp.offsets)
+    log(f"few-row experts, cf={cf}: rows per expert {rows.tolist()}")
+    assert cfg.T * 2 > 8 * 256 and (rows <= 128).sum() >= 3 and (rows > 256).sum() >= 3
+    assert np.array_equal(host_array(ax["offsets"]), res.disp.offsets)
+    assert np.array_equal(host_array(ax["dropped"]), res.disp.dropped)
+    got = moe.moe_dispatch(ax["topk_idx"], 8, cf)
+    torch.cuda.synchronize()
+    check_dispatch_equal({k: host_array(v) for k, v in got.items()}, res.disp)
+    check_close(out_as_f64(out), res.out, "bf16", f"few-row experts cf={cf}")
