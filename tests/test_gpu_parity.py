@@ -56,6 +56,43 @@ def test_router_topk(moe, name):
     check_routing(host_array(idx), host_array(w), res.routing)
 
 
+# Many tokens: the matrix-core router (bf16 x, E <= 8, from 4608 tokens).
+# Cases: the Grok-1 prefill shape; a ragged last group of 32 tokens; hidden
+# sizes whose 64-wide chunks split unevenly over the 4 waves (7 chunks: 2, 2,
+# 2, 1; 17 chunks) or leave waves without a chunk (H = 64); E = 6, 4 with
+# k = 3, 1, 4; and the vector kernel at the same token counts (float32 x,
+# E > 8) and just below the threshold.
+ROUTER_MANY = [
+    # name, T, H, E, k
+    ("grok_prefill", 8192, 6144, 8, 2),
+    ("ragged", 4608 + 17, 512, 8, 2),
+    ("h448_e6_k3", 5001, 448, 6, 3),
+    ("h64_e4_k1", 4650, 64, 4, 1),
+    ("h1088_k4", 6000, 1088, 8, 4),
+    ("f32_vector", 4608, 256, 8, 2),
+    ("e12_vector", 4608, 256, 12, 2),
+    ("below_threshold", 4607, 512, 8, 2),
+]
+
+
+@pytest.mark.parametrize("name,T,H,E,k", ROUTER_MANY, ids=[r[0] for r in ROUTER_MANY])
+def test_router_topk_many_tokens(moe, name, T, H, E, k):
+    cfg = synth.LayerConfig(f"router_{name}", T=T, H=H, F=64, E=E, k=k, seed=200 + T % 97,
+                            act="f32" if name.startswith("f32") else "bf16")
+    inp = synth.generate_host(cfg)
+    log(f"router {name} T={T} H={H} E={E} k={k}")
+    x64 = oracle.widen(inp.x, cfg.act)
+    l32, l64 = oracle.router_logits(x64, inp.wr)
+    routing = oracle.top_k_softmax(l32, l64, k)
+    d = to_device(inp)
+    idx, w, logits = moe.moe_router_topk(d["x"], d["wr"], k, return_logits=True)
+    torch.cuda.synchronize()
+    lg = host_array(logits).astype(np.float64)
+    scale = np.maximum(1.0, np.abs(l64).max(axis=1, keepdims=True))
+    assert np.max(np.abs(lg - l64) / scale) < 2e-5
+    check_routing(host_array(idx), host_array(w), routing)
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_dispatch_on_oracle_indices(moe, name):
     cfg, inp, d, res = case(name)
