@@ -513,7 +513,8 @@ def main():
                     help="skip the secondary lines (prefill, medium, int4 decode, training step)")
     ap.add_argument("--no-train", action="store_true", help="skip the training-step secondary line")
     ap.add_argument("--cpu-tokens", type=int, default=8,
-                    help="tokens in the oracle's timed sample (0 skips the CPU baselines)")
+                    help="tokens in the oracle's timed sample at decode sizes (0 skips the CPU "
+                         "baselines); workloads above 16 tokens time a 256-token sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (float32 negate: reads "
                          "and writes MIB MiB per launch) 3 times, to calibrate HBM byte counters")
@@ -637,7 +638,13 @@ def main():
     if args.cpu_tokens > 0:
         log("cpu baselines: copying the inputs to the host")
         h = host_inputs(layer)
-        result["cpu_baseline"] = cpu_baseline(layer, h, min(args.cpu_tokens, cfg.T))
+        if cfg.T > 16:
+            # MFMA-bound workloads: routing and dispatch over all T, the FFN
+            # on a 256-token sample, the full layer extrapolated
+            log(f"cpu baseline of the {cfg.name} workload (256-token sample)")
+            result["cpu_baseline"] = cpu_baseline_sampled(layer, h)
+        else:
+            result["cpu_baseline"] = cpu_baseline(layer, h, min(args.cpu_tokens, cfg.T))
         if pl is not None:
             hp = dict(h)
             hx = host_inputs_x(pl)
