@@ -58,6 +58,11 @@ SHAPES = [
     # of scale groups in one matrix and an even number in the other
     ("t5_i8_h320", 5, 320, 448, 8, 2, "bf16", "i8", None),
     ("t9_i8_f576", 9, 512, 576, 8, 2, "bf16", "i8", None),
+    # int4 double steps over long rows: gate/up at H = 8448 (66 scale groups
+    # per row), down at F = 65792 (514 groups, 257 double steps over 8 k
+    # splits: a ragged last split)
+    ("t4_i4_h8448", 4, 8448, 256, 8, 2, "bf16", "i4", None),
+    ("t4_i4_f65792", 4, 256, 65792, 8, 2, "bf16", "i4", None),
     ("t8_i4_mixed", 8, 512, 640, 8, 2, "bf16", "i4", None),
 ]
 
