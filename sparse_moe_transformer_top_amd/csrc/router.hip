@@ -25,8 +25,8 @@
 // in float32 and lo exact in bf16), and a 32x32x16 bf16 MFMA takes 32 tokens
 // against 24 columns (hi, mid, lo of 8 experts). Every product of a bf16 x and
 // a bf16 term is exact in float32, so a logit is the exact dot product up to
-// float32 accumulation, as on the vector path. The kernel then reads x once at
-// close to HBM rate.
+// float32 accumulation, as on the vector path. The kernel is then bound by
+// reading x once and each work-group's copy of the router weights (from L2).
 #include "common.h"
 #include "kernels.h"
 
@@ -191,14 +191,15 @@ __global__ __launch_bounds__(kWaves * 64) void router_topk_kernel(
 // ---------------------------------------------------------------------------
 // A work-group owns 32 tokens (one MFMA row tile) and its NW waves take the
 // hidden dimension in chunks of 64, round-robin (wave q: chunks q, q + NW,
-// ...), so neighbouring waves read neighbouring pieces of the same x rows.
-// (8 or 16 waves per work-group, or 6 or 8 chunks in flight, were slower.) Per chunk a wave (1) splits
-// the 8 x 64 router weights into hi / mid / lo and writes them to its own LDS
-// buffer as 24 rows of 64 bf16 (rows s*8 + e; 16-byte chunks XOR-swizzled by
-// (row / 2) % 8, so the MFMA's B-operand reads of 16 rows at one chunk column
-// hit 16 distinct 16-byte bank groups), (2) runs 4 MFMAs (two accumulators,
-// so consecutive MFMAs do not wait for each other) with the x rows as the A
-// operand straight from registers. x and router loads run D chunks ahead.
+// ...), so neighbouring waves read neighbouring pieces of the same x rows
+// (8 or 16 waves per work-group, or 6 or 8 chunks in flight, were slower).
+// Per chunk a wave (1) splits the 8 x 64 router weights into hi / mid / lo
+// and writes them to its own LDS buffer as 24 rows of 64 bf16 (rows s*8 + e;
+// 16-byte chunks XOR-swizzled by (row / 2) % 8, so the MFMA's B-operand reads
+// of 16 rows at one chunk column hit 16 distinct 16-byte bank groups), (2)
+// runs 4 MFMAs (two accumulators, so consecutive MFMAs do not wait for each
+// other) with the x rows as the A operand straight from registers. x and
+// router loads run D chunks ahead.
 // The waves' 32 x 24 partial sums then meet in LDS (over the split buffers)
 // and one lane per token adds them in a fixed order (wave, then hi, mid, lo),
 // so logits are deterministic.
