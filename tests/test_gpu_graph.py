@@ -2,7 +2,8 @@
 with new inputs written into the captured buffers between them, and eager
 work on the same stream in between, each equal bitwise to an eager call on
 the same inputs. Covers the decode kernels (T <= 16, token rows staged in
-LDS) and the tiled MFMA kernels, with and without a capacity limit."""
+LDS) and the tiled MFMA kernels, with and without a capacity limit, and the
+matrix-core router."""
 import numpy as np
 import pytest
 import torch
@@ -24,11 +25,21 @@ def _same(a, b):
     return torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["p_dec1", "p_bf16_dec", "p_bf16", "p_cap"])
-def test_layer_forward_graph_replays(moe, name):
+# the last case routes on the matrix-core router kernel (from 4608 tokens)
+GRAPH_CASES = ["p_dec1", "p_bf16_dec", "p_bf16", "p_cap", "many_tokens"]
+
+
+def _graph_config(name):
+    if name == "many_tokens":
+        return synth.LayerConfig("g_many_tokens", T=4700, H=512, F=256, capacity_factor=1.25,
+                                 seed=21)
     cfg = synth.get_config(name)
-    if cfg.T < 8:
-        cfg = cfg.with_(T=8)
+    return cfg.with_(T=8) if cfg.T < 8 else cfg
+
+
+@pytest.mark.parametrize("name", GRAPH_CASES)
+def test_layer_forward_graph_replays(moe, name):
+    cfg = _graph_config(name)
     log(f"graph capture {name}: T={cfg.T} cf={cfg.capacity_factor}")
     d = to_device(synth.generate_host(cfg))
     x = d["x"].clone()
