@@ -59,9 +59,10 @@ def test_router_topk(moe, name):
 # Many tokens: the matrix-core router (bf16 x, E <= 8, from 4608 tokens).
 # Cases: the Grok-1 prefill shape; a ragged last group of 32 tokens; hidden
 # sizes whose 64-wide chunks split unevenly over the 4 waves (7 chunks: 2, 2,
-# 2, 1; 17 chunks) or leave waves without a chunk (H = 64); E = 6, 4 with
-# k = 3, 1, 4; and the vector kernel at the same token counts (float32 x,
-# E > 8) and just below the threshold.
+# 2, 1; 17 chunks) or leave waves without a chunk (H = 64); E = 6, 4, 2, 1
+# with k = 3, 1, 4, 2, 1 (E = k: every expert selected; E = 1: the weight is
+# 1); and the vector kernel at the same token counts (float32 x, E > 8) and
+# just below the threshold.
 ROUTER_MANY = [
     # name, T, H, E, k
     ("grok_prefill", 8192, 6144, 8, 2),
@@ -72,6 +73,8 @@ ROUTER_MANY = [
     ("f32_vector", 4608, 256, 8, 2),
     ("e12_vector", 4608, 256, 12, 2),
     ("below_threshold", 4607, 512, 8, 2),
+    ("at_threshold_e2_k2", 4608, 320, 2, 2),
+    ("e1_k1", 4609, 128, 1, 1),
 ]
 
 
