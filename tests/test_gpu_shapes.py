@@ -63,6 +63,11 @@ SHAPES = [
     # splits: a ragged last split)
     ("t4_i4_h8448", 4, 8448, 256, 8, 2, "bf16", "i4", None),
     ("t4_i4_f65792", 4, 256, 65792, 8, 2, "bf16", "i4", None),
+    # int4 gate/up scales staged in LDS in 256-byte pieces per 16-row tile:
+    # H = 768 gives 6 groups per row, 96 scales per tile, a full and a
+    # partial piece (H = 256 above: one partial piece and three waves without
+    # a double step; H = 8448: 66 groups, past the table, read from memory)
+    ("t6_i4_h768", 6, 768, 384, 8, 2, "bf16", "i4", None),
     ("t8_i4_mixed", 8, 512, 640, 8, 2, "bf16", "i4", None),
 ]
 
