@@ -65,8 +65,11 @@ template <int WT> struct GateUpWaves { static constexpr int N = kWavesGateUp; };
 template <> struct GateUpWaves<WT_I4> { static constexpr int N = MOE_I4_GU_WAVES; };
 template <int WT> struct DownWaves { static constexpr int N = kWavesDown; };
 template <> struct DownWaves<WT_I4> { static constexpr int N = MOE_I4_DN_WAVES; };
+// int4 down: 4 k splits, so that a split's double steps (8 per wave at the
+// Grok-1 shape) repay staging its group scales in LDS (stage_scales_i4);
+// with 8 splits the staging was slower than reading the scales per step
 #ifndef MOE_I4_DOWN_SPLIT
-#define MOE_I4_DOWN_SPLIT 8
+#define MOE_I4_DOWN_SPLIT 4
 #endif
 constexpr int kDownSplit = 8;
 template <int WT> struct DownSplit { static constexpr int N = kDownSplit; };
@@ -284,15 +287,21 @@ MOE_DEV void dstep_offsets(int n0, int rows, int row_bytes, int i, int g, uint32
 // step 0 (dstep_offsets), so[t] the index of the first group scale of the
 // lane's weight row in tile t (row 16 t + i). Accumulator t NM + m holds
 // tile t of matrix m. The bases are uniform over the work-group, so each
-// load is a scalar base plus a 32-bit lane offset.
-template <int NT, int NM, int W, int kInFlight>
+// load is a scalar base plus a 32-bit lane offset. With LS the group scales
+// come from the work-group's LDS table (stage_scales_i4: tile b's row r,
+// group 2 d + h at scl[b ts + r ng + 2 (d - d_first) + h]); prep() runs once
+// the first loads are issued (every wave calls it, also one without a double
+// step).
+template <int NT, int NM, int W, int kInFlight, bool LS, typename Prep>
 MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wb)[NM],
                               const uint32_t (&wo)[NT][2], const float* const (&sb)[NM],
-                              const uint32_t (&so)[NT], int d_begin, int d_end, int wave, int i,
-                              int g, f32x4 (&acc)[NT * NM]) {
+                              const uint32_t (&so)[NT], const float* scl, int ts, int ng,
+                              int d_first, int d_begin, int d_end, int wave, int i, int g,
+                              f32x4 (&acc)[NT * NM], Prep prep) {
   constexpr int NB = NT * NM;
   constexpr uint32_t kNeg136 = 0xC308C308u;   // two bf16 -136.0
   const u32x4 cneg = {kNeg136, kNeg136, kNeg136, kNeg136};
+  bool prepped = false;
   for (int d0 = d_begin + wave; d0 < d_end; d0 += W * kInFlight) {
     u32x4 bv[kInFlight][NB][2];
     u32x4 av[kInFlight][2][4];
@@ -308,7 +317,8 @@ MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wb)[NM],
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               bv[u][t * NM + m][h] = ld16_nt(wb[m] + (wo[t][h] + (uint32_t)d * 128u));
-              sc[u][t * NM + m][h] = sb[m][so[t] + 2u * (uint32_t)d + (uint32_t)h];
+              if constexpr (!LS)
+                sc[u][t * NM + m][h] = sb[m][so[t] + 2u * (uint32_t)d + (uint32_t)h];
             }
           }
         }
@@ -320,9 +330,20 @@ MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wb)[NM],
         }
       }
     }
+    if (!prepped) {
+      prep();
+      prepped = true;
+    }
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       if (d0 + W * u < d_end) {
+        if constexpr (LS) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              sc[u][b][h] = scl[b * ts + i * ng + 2 * (d0 + W * u - d_first) + h];
+        }
         u32x4 op[NB][2];
 #pragma unroll
         for (int b = 0; b < NB; ++b) dstep_operands(bv[u][b][0], bv[u][b][1], i, op[b][0], op[b][1]);
@@ -349,7 +370,7 @@ MOE_DEV void stream_dsteps_i4(const uint16_t* arow, const char* const (&wb)[NM],
         }
       }
     }
-  }
+  }  if (!prepped) prep();
 }
 
 // The same double steps as stream_dsteps_i4, software-pipelined without a
@@ -473,31 +494,32 @@ MOE_DEV void lds_dma4(const void* g, uint32_t lds) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 MOE_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void_t*)p; }
 
-// The group scales of the int4 gate/up work-group's NB 16-row tiles, staged
-// in LDS by direct-to-LDS loads at the start of the kernel. Read from global
-// memory at each double step, a tile's 2 scales of 16 rows touch 16 cache
-// lines for 128 useful bytes, about as many L2 requests as the weight stream
-// itself; staged once, the stream takes ~10% less time at the Grok-1 shape.
-// (In the down projection a work-group's k split holds two double steps per
-// wave, too few to repay the staging: measured slower, so it keeps reading
-// its scales from memory.) A tile's 16 rows of G scales are consecutive in
-// memory (the tile's rows are consecutive), so they are copied as 256-byte
-// pieces (64 lanes x 4 bytes) into a table with tile stride ts = 16 G
-// rounded up to 64 floats; lanes past the tile's last scale read that scale
-// again (in bounds) into the stride's padding. The pieces go round-robin
-// over the waves; no wait here (the stream's prep waits and synchronises).
+// The int4 group scales a work-group's NB 16-row tiles need, staged in LDS
+// by direct-to-LDS loads at the start of the kernel. Read from global memory
+// at each double step, a tile's 2 scales of 16 rows touch 16 cache lines for
+// 128 useful bytes, about as many L2 requests as the weight stream itself;
+// staged once, the gate/up stream takes ~10% less time and the down
+// projection ~7% at the Grok-1 shape. Tile b's row r holds ng groups (the
+// work-group's range: all G of a gate/up row, a k split's of a down row;
+// tile0[b] points at row 0's first group of the range, rows G apart) at
+// scl[b ts + r ng + c], ts = 16 ng rounded up to 64 floats. The table is
+// copied in 256-byte pieces (64 lanes x 4 bytes, each lane its own source
+// address; for a whole row, 16 consecutive rows are contiguous), round-robin
+// over the waves; lanes past a tile's last scale read that scale again (in
+// bounds) into the stride's padding. No wait here: the stream's prep waits
+// for the loads and synchronises the block.
 constexpr int kI4ScaleTable = 1024;   // floats per tile in the table: 16 rows of <= 64 groups
-__host__ __device__ inline int scale_tile_stride(int G) { return (16 * G + 63) / 64 * 64; }
+__host__ __device__ inline int scale_tile_stride(int ng) { return (16 * ng + 63) / 64 * 64; }
 // s_waitcnt vmcnt(0), leaving the other counters untouched
 MOE_DEV void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00); }
 template <int NB, int W>
-MOE_DEV void stage_scales_i4(float* scl, int ts, int G, const float* const (&tile0)[NB],
+MOE_DEV void stage_scales_i4(float* scl, int ts, int ng, int G, const float* const (&tile0)[NB],
                              int wave, int lane) {
-  const int pieces = ts / 64, n = 16 * G;
+  const int pieces = ts / 64, n = 16 * ng;
   for (int q = wave; q < NB * pieces; q += W) {
-    const int b = q / pieces, c = (q - b * pieces) * 64 + lane;
-    lds_dma4(tile0[b] + min(c, n - 1),
-             __builtin_amdgcn_readfirstlane(lds_addr(scl) + (uint32_t)(b * ts + c - lane) * 4u));
+    const int b = q / pieces, f = (q - b * pieces) * 64 + lane, fc = min(f, n - 1);
+    lds_dma4(tile0[b] + (ng == G ? fc : (fc / ng) * G + fc % ng),
+             __builtin_amdgcn_readfirstlane(lds_addr(scl) + (uint32_t)(b * ts + f - lane) * 4u));
   }
 }
 
@@ -703,7 +725,7 @@ __global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64, kI4GuWavesPerSimd) void
       const float* tile0[2 * NT];
 #pragma unroll
       for (int b = 0; b < 2 * NT; ++b) tile0[b] = sb[b % 2] + (int64_t)(n0 + 16 * (b / 2)) * G;
-      stage_scales_i4<2 * NT, kWaves>(scl, ts, G, tile0, wave, lane);
+      stage_scales_i4<2 * NT, kWaves>(scl, ts, G, G, tile0, wave, lane);
     }
     auto prep = [&]() {
       if constexpr (LS) {   // the staged scales (and the first step's loads) landed
@@ -740,12 +762,13 @@ __global__ __launch_bounds__(GateUpWaves<WT_I4>::N * 64, kI4GuWavesPerSimd) void
   }
 }
 
-template <int NT>
+template <int NT, bool LS>
 __global__ __launch_bounds__(DownWaves<WT_I4>::N * 64) void down_decode_i4_kernel(FfnArgs a) {
   constexpr int kWaves = DownWaves<WT_I4>::N;
   constexpr int kSplit = DownSplit<WT_I4>::N;
   static_assert(NT <= kWaves, "one wave per tile in the epilogue");
   __shared__ float red[kWaves][NT][4][64];
+  __shared__ __align__(16) float scl[LS ? NT * kI4ScaleTable : 1];
   const int groups = (a.H + 16 * NT - 1) / (16 * NT);
   const int split = blockIdx.x % kSplit;
   const int tile = blockIdx.x / kSplit;
@@ -779,10 +802,26 @@ __global__ __launch_bounds__(DownWaves<WT_I4>::N * 64) void down_decode_i4_kerne
       dstep_offsets(n0 + 16 * t, a.H, a.F / 2, i, g, wo[t]);
       so[t] = (uint32_t)min(n0 + 16 * t + i, a.H - 1) * (uint32_t)(a.F / 128);
     }
+    // the split's groups [2 kb, 2 ke) of the tiles' rows (at most 64: checked at launch)
+    const int G = a.F / 128, ng = 2 * (ke - kb), ts = scale_tile_stride(ng);
+    if constexpr (LS) {
+      if (ng > 0) {
+        const float* tile0[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) tile0[t] = sb[0] + (int64_t)(n0 + 16 * t) * G + 2 * kb;
+        stage_scales_i4<NT, kWaves>(scl, ts, ng, G, tile0, wave, lane);
+      }
+    }
+    auto prep = [&]() {
+      if constexpr (LS) {   // the staged scales (and the first step's loads) landed
+        wait_vmcnt0();
+        __syncthreads();
+      }
+    };
     // (the pipelined stream, stream_dsteps_i4_roll, needs 163 VGPRs here
     // against 121, which halves the work-groups per CU: measured slower)
-    stream_dsteps_i4<NT, 1, kWaves, (InFlight<WT_I4, 1>::N + 1) / 2>(arow, wb, wo, sb, so, kb, ke,
-                                                                     wave, i, g, acc);
+    stream_dsteps_i4<NT, 1, kWaves, (InFlight<WT_I4, 1>::N + 1) / 2, LS>(
+        arow, wb, wo, sb, so, scl, ts, ng, kb, kb, ke, wave, i, g, acc, prep);
   } else {
     split_range(a.F / 128, kSplit, split, kb, ke);
     stream_steps_i4<NT, kWaves, InFlight<WT_I4, 1>::N>(arow, wrow, srow, kb, ke, wave, g, acc);
@@ -873,9 +912,15 @@ hipError_t launch_down_decode(const FfnArgs& a, Wt wt, hipStream_t s) {
     nsplit = DownSplit<WT_I8>::N;
   } else if (wt == WT_I4) {
     const unsigned groups = (unsigned)((a.H + 16 * kI4DownTiles - 1) / (16 * kI4DownTiles));
-    hipLaunchKernelGGL(down_decode_i4_kernel<kI4DownTiles>,
-                       dim3((unsigned)a.E * groups * DownSplit<WT_I4>::N),
-                       dim3(DownWaves<WT_I4>::N * 64), 0, s, a);
+    const dim3 gd((unsigned)a.E * groups * DownSplit<WT_I4>::N);
+    // a split's double steps: at most ceil(F / 256 / splits), two groups each
+    const int dsteps = (a.F / 256 + DownSplit<WT_I4>::N - 1) / DownSplit<WT_I4>::N;
+    if ((a.F / 128) % 2 == 0 && scale_tile_stride(2 * dsteps) <= kI4ScaleTable)
+      hipLaunchKernelGGL((down_decode_i4_kernel<kI4DownTiles, true>), gd,
+                         dim3(DownWaves<WT_I4>::N * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((down_decode_i4_kernel<kI4DownTiles, false>), gd,
+                         dim3(DownWaves<WT_I4>::N * 64), 0, s, a);
     nsplit = DownSplit<WT_I4>::N;
   } else {
     hipLaunchKernelGGL(down_decode_kernel<WT_BF16>, grid(DownSplit<WT_BF16>::N),
